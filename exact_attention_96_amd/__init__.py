@@ -1,0 +1,1 @@
+"""Exact scaled-dot-product attention forward for MI355X (gfx950)."""

@@ -1,0 +1,106 @@
+"""Seeded synthetic attention inputs.
+
+This module only draws random tensors; it holds none of the attention
+arithmetic.  The oracle and the HIP path both consume what it returns, so a
+parity check always compares the two on identical inputs.
+
+Recipe (one CPU generator per call, seeded):
+  Q, K, V are drawn in that order, each ``torch.randn(B, H, N, d, float32) * std``;
+  for the "spiky" workload, ``round(0.01 * B*H*N)`` key rows picked by
+  ``torch.randperm(B*H*N)`` over the flattened (b, h, n) rows are then
+  multiplied by 8 (exact in every dtype used, being a power of two), which makes
+  the running row maximum jump and exercises the rescaling of the online
+  softmax; finally each tensor is rounded to the working dtype (round to
+  nearest even).  The scale is 1/sqrt(d) rounded to fp32, the value of the
+  naive-attention module of "PyTorch profiling part 3: attention" (section
+  "朴素注意力").
+
+The pages publish no benchmark dataset; these workloads stand in for the
+attention shapes they discuss (long causal sequences, short many-head
+batches).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f32" | "f16" | "bf16"
+    causal: bool
+    std: float = 1.0
+    spiky_frac: float = 0.0   # fraction of key rows multiplied by 8
+    seed: int = 0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to fp32 (the value the kernel receives)."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def elt(self) -> int:
+        return torch.tensor([], dtype=self.torch_dtype).element_size()
+
+    @property
+    def io_bytes(self) -> int:
+        """Algorithmic bytes: read Q, K, V once, write O once (dtype) and lse once (fp32)."""
+        return 4 * self.B * self.H * self.N * self.d * self.elt + 4 * self.B * self.H * self.N
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads (seeds 1..5).  "c3" is the headline one.
+WORKLOADS = {
+    "c1": Workload("c1_f32_noncausal_b1h1n128d64", 1, 1, 128, 64, "f32", False, seed=1),
+    "c2": Workload("c2_bf16_causal_b4h16n2048d64", 4, 16, 2048, 64, "bf16", True, seed=2),
+    "c3": Workload("c3_bf16_causal_b2h32n8192d128", 2, 32, 8192, 128, "bf16", True, seed=3),
+    "c4": Workload("c4_f16_noncausal_b16h16n512d64_spiky", 16, 16, 512, 64, "f16", False,
+                   std=0.5, spiky_frac=0.01, seed=4),
+    "c5": Workload("c5_bf16_causal_b1h8n32768d128", 1, 8, 32768, 128, "bf16", True, seed=5),
+}
+HEADLINE = "c3"
+
+
+def make_inputs(w: Workload, seed: int | None = None):
+    """Q, K, V (CPU tensors in w's dtype, shape [B, H, N, d]) for workload w."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = torch.randn(shape, dtype=torch.float32, generator=g) * w.std
+    k = torch.randn(shape, dtype=torch.float32, generator=g) * w.std
+    v = torch.randn(shape, dtype=torch.float32, generator=g) * w.std
+    if w.spiky_frac > 0:
+        rows = w.B * w.H * w.N
+        n_spiky = int(round(w.spiky_frac * rows))
+        idx = torch.randperm(rows, generator=g)[:n_spiky]
+        k.view(rows, w.d)[idx] *= 8.0
+    dt = w.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+def random_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int, std: float = 1.0):
+    """Q, K, V for an ad-hoc shape (parity sweeps), same recipe as make_inputs."""
+    w = Workload("adhoc", B, H, N, d, dtype, False, std=std, seed=seed)
+    return make_inputs(w)

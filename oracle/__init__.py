@@ -1,0 +1,151 @@
+"""fp64 CPU attention oracle — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``exact_attention_96_amd``) and neither imports the other.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, OpenMP over rows): the
+literal definition of scaled-dot-product attention with a causal lower-
+triangle mask, softmax over keys and the per-row log-sum-exp, following
+"Understand FlashAttention" (nothiny.github.io), sections "前向传播" and
+"附：数值稳定的logsumexp(L)推导", and "PyTorch profiling part 3: attention",
+section "朴素注意力" (naive attention).  This module only marshals arrays.
+
+Pins (tests/test_oracle.py) tie it to facts the pages and the mathematics fix;
+every function here is pinned (none is "parity unpinned").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "attn_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(verbose: bool = False, src: str = SRC, out: str = LIB, werror: bool = True) -> str:
+    """Compile attn_oracle.c with gcc into a shared library (always recompiles).
+
+    Plain -O2, no -ffast-math (keeps IEEE semantics and the written summation
+    order) and no -march=native (the library must run on other x86 hosts).
+    """
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-Wall", "-Wextra"] + (["-Werror"] if werror else []) + [src, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class OracleLib:
+    """ctypes handle on one build of attn_oracle.c (the default one, or a test build)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            raise RuntimeError(f"oracle library missing: {path} (run oracle.build())")
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_attn_fwd_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                            ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_fwd_f64.restype = ctypes.c_int
+        lib.oracle_attn_rows_f64.argtypes = [dp, dp, dp, i64, i64, ctypes.c_double,
+                                             ctypes.c_int, ctypes.POINTER(i64), i64, dp, dp]
+        lib.oracle_attn_rows_f64.restype = ctypes.c_int
+        lib.oracle_attn_dense_f64.argtypes = [dp, dp, i64, i64, ctypes.c_double,
+                                              ctypes.c_int, dp, dp]
+        lib.oracle_attn_dense_f64.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def attn_fwd(self, q, k, v, scale: float, causal: bool):
+        """O, lse for q, k, v of shape [B, H, N, d] (any float dtype, widened exactly)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one [B, H, N, d] shape")
+        B, H, N, d = q.shape
+        o = np.empty_like(q)
+        lse = np.empty((B, H, N), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                          B, H, N, d, float(scale), int(bool(causal)))
+        if rc:
+            raise RuntimeError(f"oracle_attn_fwd_f64 failed with status {rc}")
+        return o, lse
+
+    def attn_rows(self, q, k, v, scale: float, causal: bool, rows):
+        """O[rows], lse[rows] for ONE head: q, k, v of shape [N, d]."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 2 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one [N, d] shape")
+        N, d = q.shape
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        o = np.empty((rows.size, d), dtype=np.float64)
+        lse = np.empty((rows.size,), dtype=np.float64)
+        rc = self.lib.oracle_attn_rows_f64(
+            _ptr(q), _ptr(k), _ptr(v), N, d, float(scale), int(bool(causal)),
+            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size, _ptr(o), _ptr(lse))
+        if rc:
+            raise RuntimeError(f"oracle_attn_rows_f64 failed with status {rc}")
+        return o, lse
+
+    def attn_dense(self, q, k, scale: float, causal: bool):
+        """Dense S (scaled, masked to -inf) and P = softmax(S) for ONE head [N, d]."""
+        q, k = _f64(q), _f64(k)
+        if q.ndim != 2 or q.shape != k.shape:
+            raise ValueError("q, k must share one [N, d] shape")
+        N, d = q.shape
+        S = np.empty((N, N), dtype=np.float64)
+        P = np.empty((N, N), dtype=np.float64)
+        rc = self.lib.oracle_attn_dense_f64(_ptr(q), _ptr(k), N, d, float(scale),
+                                            int(bool(causal)), _ptr(S), _ptr(P))
+        if rc:
+            raise RuntimeError(f"oracle_attn_dense_f64 failed with status {rc}")
+        return S, P
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of a torch tensor or array to a C-contiguous fp64 array."""
+    if hasattr(x, "detach"):  # torch tensor (any float dtype, CPU or GPU)
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    global _default
+    if _default is None:
+        _default = OracleLib(LIB)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool):
+    return default().attn_fwd(q, k, v, scale, causal)
+
+
+def attn_rows(q, k, v, scale: float, causal: bool, rows):
+    return default().attn_rows(q, k, v, scale, causal, rows)
+
+
+def attn_dense(q, k, scale: float, causal: bool):
+    return default().attn_dense(q, k, scale, causal)

@@ -1,0 +1,225 @@
+/*
+ * Reference attention forward in fp64 — TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the oracle that the GPU path is checked against.  Only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * load it.  It shares no source, header, helper or constant with the HIP
+ * library, and nothing in the product path may call it.
+ *
+ * What it computes is the plain definition of scaled-dot-product attention,
+ * written out literally, with no tiling, no online softmax and no reordering:
+ *
+ *   "Understand FlashAttention" (nothiny.github.io), section "Attention 前向和
+ *   反向传播公式 / 前向传播": S = Q K^T, P = softmax(S), O = P V, with
+ *   Q, K, V in R^{N x d}.
+ *
+ *   "PyTorch profiling part 3: attention" (Hugging Face blog, Chinese
+ *   translation), section "朴素注意力" (naive attention), its five steps:
+ *   scores = q k^T; scores *= scale; masked entries set to -inf;
+ *   softmax over the key axis; out = attn v.  The causal mask is the
+ *   lower triangle (section "构建因果掩码": ones -> tril), so key j is
+ *   allowed for query i iff j <= i.
+ *
+ *   "Understand FlashAttention", section "数值稳定的 Softmax": softmax is
+ *   evaluated as e^{x_i - m} / sum_j e^{x_j - m} with m the row max, and the
+ *   section "附：数值稳定的logsumexp(L)推导" defines the per-row
+ *   log-sum-exp L_i = m_i + log(sum_j e^{S_ij - m_i}) (natural log).
+ *
+ * Readings taken where the pages are silent:
+ *   - the scale multiplies the raw dot product before masking (naive
+ *     attention, steps 1-3);
+ *   - a row with every key masked (plain softmax would give 0/0) yields
+ *     o = 0 and lse = -inf, the "safe softmax" reading of that page's section
+ *     "安全 softmax".  The library's boundary (equal query and key lengths,
+ *     diagonal kept) never produces such a row.
+ *
+ * Every row materialises its whole score row s[0..N) in fp64; inputs are the
+ * exact values the GPU sees, widened to double by the caller.  Summation is a
+ * plain left-to-right loop, so results are deterministic.  Rows are
+ * independent and are spread over OpenMP threads.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One query row of one head.
+ *   q_i  : [d]      the query row
+ *   k, v : [N, d]   keys and values of the head, row-major
+ *   s    : [N]      scratch for the score row (written)
+ *   o_i  : [d]      output row (written)
+ *   lse_i: scalar   log-sum-exp of the scaled, masked score row (written)
+ */
+static void attention_row(const double *q_i, const double *k, const double *v,
+                          int64_t N, int64_t d, double scale, int causal,
+                          int64_t i, double *s, double *o_i, double *lse_i)
+{
+    /* naive attention steps 1-2: scores = (q . k_j) * scale */
+    for (int64_t j = 0; j < N; ++j) {
+        const double *k_j = k + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += q_i[c] * k_j[c];
+        s[j] = dot * scale;
+    }
+    /* step 3: causal mask (lower triangle, diagonal kept) */
+    if (causal)
+        for (int64_t j = i + 1; j < N; ++j)
+            s[j] = -INFINITY;
+
+    /* step 4: numerically stable softmax, m = row max, l = sum e^{s-m} */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j)
+        if (s[j] > m)
+            m = s[j];
+
+    for (int64_t c = 0; c < d; ++c)
+        o_i[c] = 0.0;
+    if (m == -INFINITY) { /* every key masked: safe-softmax reading */
+        *lse_i = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        s[j] = exp(s[j] - m); /* s now holds the unnormalised weights */
+        l += s[j];
+    }
+    /* step 5: out = P v with P_ij = e^{s_ij - m} / l */
+    for (int64_t j = 0; j < N; ++j) {
+        const double p = s[j] / l;
+        const double *v_j = v + j * d;
+        for (int64_t c = 0; c < d; ++c)
+            o_i[c] += p * v_j[c];
+    }
+    *lse_i = m + log(l);
+}
+
+/* Returns 0 on success, 1 on an invalid argument, 2 when scratch memory
+ * cannot be allocated. */
+static int check_args(const void *q, const void *k, const void *v,
+                      const void *o, const void *lse, int64_t N, int64_t d,
+                      int causal)
+{
+    if (!q || !k || !v || !o || !lse) return 1;
+    if (N < 1 || d < 1) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    return 0;
+}
+
+/* Full forward for all heads.
+ *   q, k, v : [B, H, N, d] row-major fp64
+ *   o       : [B, H, N, d] (written)
+ *   lse     : [B, H, N]    (written)
+ */
+int oracle_attn_fwd_f64(const double *q, const double *k, const double *v,
+                        double *o, double *lse, int64_t B, int64_t H,
+                        int64_t N, int64_t d, double scale, int causal)
+{
+    int rc = check_args(q, k, v, o, lse, N, d, causal);
+    if (rc) return rc;
+    if (B < 1 || H < 1) return 1;
+    const int64_t rows = B * H * N;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!s) continue;
+            const int64_t head = r / N, i = r % N;
+            const int64_t base = head * N * d;
+            attention_row(q + base + i * d, k + base, v + base, N, d, scale,
+                          causal, i, s, o + r * d, lse + r);
+        }
+        free(s);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Selected query rows of ONE head (used to check large problems row by row).
+ *   q, k, v : [N, d] of the head
+ *   rows    : [nrows] query indices in [0, N)
+ *   o       : [nrows, d] (written);  lse : [nrows] (written)
+ */
+int oracle_attn_rows_f64(const double *q, const double *k, const double *v,
+                         int64_t N, int64_t d, double scale, int causal,
+                         const int64_t *rows, int64_t nrows, double *o,
+                         double *lse)
+{
+    int rc = check_args(q, k, v, o, lse, N, d, causal);
+    if (rc) return rc;
+    if (!rows || nrows < 0) return 1;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= N) return 1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < nrows; ++t) {
+            if (!s) continue;
+            const int64_t i = rows[t];
+            attention_row(q + i * d, k, v, N, d, scale, causal, i, s,
+                          o + t * d, lse + t);
+        }
+        free(s);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Dense intermediates of ONE head, for small N:
+ *   S : [N, N] scaled scores with masked entries set to -inf (written)
+ *   P : [N, N] softmax rows (written)
+ */
+int oracle_attn_dense_f64(const double *q, const double *k, int64_t N,
+                          int64_t d, double scale, int causal, double *S,
+                          double *P)
+{
+    if (!q || !k || !S || !P || N < 1 || d < 1) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    for (int64_t i = 0; i < N; ++i) {
+        double *s = S + i * N, *p = P + i * N;
+        for (int64_t j = 0; j < N; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dot += q[i * d + c] * k[j * d + c];
+            s[j] = dot * scale;
+            if (causal && j > i) s[j] = -INFINITY;
+        }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j)
+            if (s[j] > m) m = s[j];
+        if (m == -INFINITY) {
+            for (int64_t j = 0; j < N; ++j) p[j] = 0.0;
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            p[j] = exp(s[j] - m);
+            l += p[j];
+        }
+        for (int64_t j = 0; j < N; ++j) p[j] /= l;
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region of this library will use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

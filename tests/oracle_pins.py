@@ -1,0 +1,336 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by the mathematics.
+
+Each ``pin_*`` takes an oracle handle (``oracle.OracleLib``) and raises
+AssertionError when the oracle disagrees with the fact it pins.  The same
+battery runs against the real oracle (tests/test_oracle.py) and against
+deliberately broken builds of it (tests/test_oracle_mutants.py), which shows
+that a plausible slip anywhere in the oracle fails at least one pin.
+
+Sources (pages cited by title and section):
+  [FA]  "Understand FlashAttention" (nothiny.github.io)
+        - "数值稳定的 Softmax": softmax(x)_i = e^{x_i-m} / sum_j e^{x_j-m}
+        - "关键统计量": per-row m (row max) and l (sum of e^{x-m})
+        - "两块情况的完整推导", steps 1-8: the blockwise (online) recurrence
+        - "前向传播": S = Q K^T, P = softmax(S), O = P V
+        - "附：数值稳定的logsumexp(L)推导": L_i = log sum_j e^{S_ij} = m_i + log l_i
+  [PT]  "PyTorch profiling part 3: attention" (Hugging Face blog, Chinese translation)
+        - "朴素注意力": scores = q k^T, times scale, masked to -inf, softmax, times v
+        - "缩放点积注意力" / "那么 math 后端有什么用？": torch's SDPA math path is a
+          plain decomposition of the same operation (used as an independent library)
+        - "构建因果掩码": the causal mask is the lower triangle (tril), key j <= query i
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(a - b))
+    worst = float(np.max(err)) if err.size else 0.0
+    assert np.all(np.isfinite(err)) and worst <= tol, f"{what}: max err {worst:.3e} > {tol:.1e}"
+
+
+def _one_head(orc, q, k, v, scale, causal):
+    o, lse = orc.attn_fwd(q[None, None], k[None, None], v[None, None], scale, causal)
+    return o[0, 0], lse[0, 0]
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_golden_hand_examples(orc):
+    """Hand-derived closed forms ([FA] 前向传播 + logsumexp appendix, [PT] 朴素注意力, 构建因果掩码)."""
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    for ex in data["examples"]:
+        q, k, v = (np.array(ex[n], dtype=np.float64) for n in ("q", "k", "v"))
+        o, lse = _one_head(orc, q, k, v, ex["scale"], ex["causal"])
+        _close(o, np.array([[float(x) for x in r] for r in ex["o"]]), 1e-14, ex["name"] + " o")
+        _close(lse, np.array([float(x) for x in ex["lse"]]), 1e-14, ex["name"] + " lse")
+
+
+def _decimal_attention(q, k, v, scale, causal):
+    """Brute force in 40-digit decimal arithmetic: the [PT] naive-attention steps."""
+    getcontext().prec = 40
+    N, d = len(q), len(q[0])
+    sc = Decimal(scale)
+    S, P, O, L = [], [], [], []
+    for i in range(N):
+        srow = []
+        for j in range(N):
+            if causal and j > i:
+                srow.append(None)
+            else:
+                dot = sum(Decimal(q[i][c]) * Decimal(k[j][c]) for c in range(d))
+                srow.append(dot * sc)
+        m = max(x for x in srow if x is not None)
+        w = [Decimal(0) if x is None else (x - m).exp() for x in srow]
+        l = sum(w)
+        prow = [x / l for x in w]
+        orow = [sum(prow[j] * Decimal(v[j][c]) for j in range(N)) for c in range(d)]
+        S.append(srow)
+        P.append(prow)
+        O.append(orow)
+        L.append(m + l.ln())
+    return S, P, O, L
+
+
+def pin_bruteforce_decimal(orc):
+    """Tiny integer inputs (scores exact in fp64) against a 40-digit brute force."""
+    rng = np.random.default_rng(1234)
+    for trial in range(40):
+        N = int(rng.integers(1, 5))
+        d = int(rng.integers(1, 3))
+        hi = 2 if trial < 30 else 30  # the last trials have logits up to ~900
+        q = rng.integers(-hi, hi + 1, size=(N, d)).astype(np.float64)
+        k = rng.integers(-hi, hi + 1, size=(N, d)).astype(np.float64)
+        v = rng.integers(-2, 3, size=(N, d)).astype(np.float64)
+        causal = bool(trial % 2)
+        scale = 0.5
+        S_ref, P_ref, O_ref, L_ref = _decimal_attention(q.tolist(), k.tolist(), v.tolist(),
+                                                        scale, causal)
+        S, P = orc.attn_dense(q, k, scale, causal)
+        for i in range(N):
+            for j in range(N):
+                want = -math.inf if S_ref[i][j] is None else float(S_ref[i][j])
+                assert S[i, j] == want, f"S[{i},{j}] = {S[i, j]} != {want} (trial {trial})"
+        _close(P, np.array([[float(x) for x in r] for r in P_ref]), 1e-15, f"P trial {trial}")
+        o, lse = _one_head(orc, q, k, v, scale, causal)
+        _close(o, np.array([[float(x) for x in r] for r in O_ref]), 1e-14, f"O trial {trial}")
+        _close(lse, np.array([float(x) for x in L_ref]), 1e-13, f"lse trial {trial}")
+
+
+def pin_two_keys_sigmoid(orc):
+    """N = 2: row 1 is a two-way softmax, o_1 = sig(s11-s10) v1 + sig(s10-s11) v0,
+    lse_1 = log(e^{s10} + e^{s11}) ([FA] logsumexp appendix)."""
+    rng = np.random.default_rng(7)
+    for causal in (False, True):
+        q, k, v = rng.standard_normal((3, 2, 5))
+        scale = 0.37
+        o, lse = _one_head(orc, q, k, v, scale, causal)
+        s10, s11 = scale * (q[1] @ k[0]), scale * (q[1] @ k[1])
+        sig = 1.0 / (1.0 + math.exp(-(s11 - s10)))
+        _close(o[1], sig * v[1] + (1 - sig) * v[0], 1e-14, "o_1")
+        mx = max(s10, s11)
+        _close(lse[1], mx + math.log(math.exp(s10 - mx) + math.exp(s11 - mx)), 1e-14, "lse_1")
+        if causal:  # row 0 sees key 0 alone
+            assert np.array_equal(o[0], v[0]) and lse[0] == scale * (q[0] @ k[0])
+
+
+def pin_zero_query(orc):
+    """Q = 0 makes every allowed score 0: uniform weights over exactly the allowed keys.
+    Causal: o_i = mean(v_0..v_i), lse_i = log(i+1); non-causal: mean(V), log N."""
+    rng = np.random.default_rng(11)
+    N, d = 37, 5
+    q = np.zeros((N, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    o, lse = _one_head(orc, q, k, v, 0.125, True)
+    _close(o, np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None], 1e-14, "causal mean")
+    _close(lse, np.log(np.arange(1, N + 1)), 1e-14, "causal log(i+1)")
+    o, lse = _one_head(orc, q, k, v, 0.125, False)
+    _close(o, np.broadcast_to(v.mean(axis=0), (N, d)), 1e-14, "mean")
+    _close(lse, np.full(N, math.log(N)), 1e-14, "log N")
+
+
+def pin_causal_row0_and_single_key(orc):
+    """Causal row 0 attends to key 0 only: o_0 = v_0 exactly, lse_0 = s_00 exactly.
+    N = 1 (either mode) is the same situation."""
+    rng = np.random.default_rng(3)
+    q, k, v = rng.standard_normal((3, 9, 4))
+    o, lse = _one_head(orc, q, k, v, 0.5, True)
+    assert np.array_equal(o[0], v[0]), "causal o_0 != v_0"
+    assert lse[0] == (q[0] @ k[0]) * 0.5, "causal lse_0 != s_00"
+    for causal in (False, True):
+        o, lse = _one_head(orc, q[:1], k[:1], v[:1], 0.5, causal)
+        assert np.array_equal(o[0], v[0]) and lse[0] == (q[0] @ k[0]) * 0.5
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_normalization(orc):
+    """Softmax rows sum to 1 ([FA] 数值稳定的 Softmax); a constant V gives that constant;
+    sum_j e^{S_ij - L_i} = 1 ([FA] 为什么保存 logsumexp: P_ij = e^{S_ij - L_i})."""
+    rng = np.random.default_rng(5)
+    for causal in (False, True):
+        N, d = 50, 8
+        q, k = rng.standard_normal((2, N, d)) * 2
+        S, P = orc.attn_dense(q, k, 0.3, causal)
+        _close(P.sum(axis=1), np.ones(N), 1e-14 * N, "row sums")
+        if causal:
+            assert np.all(P[np.triu_indices(N, 1)] == 0.0), "masked weights not zero"
+        c = rng.standard_normal(d)
+        v = np.broadcast_to(c, (N, d)).copy()
+        o, lse = _one_head(orc, q, k, v, 0.3, causal)
+        _close(o, v, 1e-14, "constant V")
+        _close(np.exp(S - lse[:, None]).sum(axis=1), np.ones(N), 1e-13, "sum e^{S-L}")
+        vr = rng.standard_normal((N, d))
+        o, _ = _one_head(orc, q, k, vr, 0.3, causal)
+        _close(o, P @ vr, 1e-13, "O = P V")
+
+
+def _blockwise(q, k, v, scale, causal, bounds):
+    """[FA] 两块情况的完整推导 applied block after block (steps 1-7 per key block,
+    step 8 once), written independently of the oracle, all query rows at once."""
+    N, d = q.shape
+    m = np.full(N, -np.inf)
+    l = np.zeros(N)
+    acc = np.zeros((N, d))
+    rows = np.arange(N)[:, None]
+    for a, b in bounds:
+        S = (q @ k[a:b].T) * scale
+        if causal:
+            S = np.where(np.arange(a, b)[None, :] > rows, -np.inf, S)
+        m_new = np.maximum(m, S.max(axis=1))
+        m_use = np.where(np.isinf(m_new), 0.0, m_new)
+        alpha = np.exp(m - m_use)
+        p = np.exp(S - m_use[:, None])
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ v[a:b]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
+
+
+def pin_online_recurrence(orc):
+    """The blockwise m/l/O rescaling equals the full softmax ([FA] steps 5-8), for
+    random block partitions (size-1 blocks included) and large dynamic range."""
+    rng = np.random.default_rng(99)
+    for trial in range(12):
+        N = int(rng.integers(1, 90))
+        d = int(rng.integers(1, 20))
+        q, k, v = rng.standard_normal((3, N, d))
+        k[rng.random(N) < 0.1] *= 8.0  # spiky keys: the running max jumps
+        if trial % 3 == 0:
+            cuts = np.arange(1, N)  # every block has one key
+        else:
+            cuts = np.sort(rng.choice(np.arange(1, N), size=min(N - 1, int(rng.integers(0, 8))),
+                                      replace=False)) if N > 1 else np.array([], dtype=int)
+        edges = [0] + [int(c) for c in cuts] + [N]
+        bounds = list(zip(edges[:-1], edges[1:]))
+        causal = bool(trial % 2)
+        o_ref, lse_ref = _blockwise(q, k, v, 0.7, causal, bounds)
+        o, lse = _one_head(orc, q, k, v, 0.7, causal)
+        _close(o, o_ref, 1e-12, f"online O trial {trial}")
+        _close(lse, lse_ref, 1e-12, f"online lse trial {trial}")
+
+
+def pin_shift_invariance(orc):
+    """Adding the same constant to every score of a row leaves P (hence O) unchanged and
+    shifts L by that constant ([FA] 数值稳定的 Softmax)."""
+    rng = np.random.default_rng(21)
+    N, d = 40, 6
+    q, k, v = rng.standard_normal((3, N, d))
+    c = 3.25
+    q2 = np.concatenate([q, np.ones((N, 1))], axis=1)
+    k2 = np.concatenate([k, np.full((N, 1), c)], axis=1)
+    v2 = np.concatenate([v, np.full((N, 1), -2.0)], axis=1)
+    for causal in (False, True):
+        o, lse = _one_head(orc, q, k, v, 0.5, causal)
+        o2, lse2 = _one_head(orc, q2, k2, v2, 0.5, causal)
+        _close(o2[:, :d], o, 1e-13, "shift O")
+        _close(o2[:, d], np.full(N, -2.0), 1e-14, "shift constant column")
+        _close(lse2, lse + 0.5 * c, 1e-13, "shift lse")
+
+
+def pin_permutation(orc):
+    """Non-causal: permuting K and V rows together leaves O and L unchanged; permuting
+    Q rows permutes O rows.  Causal: row i equals the last row of the non-causal
+    problem restricted to keys 0..i (the lower-triangle mask, [PT] 构建因果掩码)."""
+    rng = np.random.default_rng(8)
+    N, d = 33, 7
+    q, k, v = rng.standard_normal((3, N, d))
+    o, lse = _one_head(orc, q, k, v, 0.4, False)
+    pk = rng.permutation(N)
+    o2, lse2 = _one_head(orc, q, k[pk], v[pk], 0.4, False)
+    _close(o2, o, 1e-13, "perm KV O")
+    _close(lse2, lse, 1e-13, "perm KV lse")
+    pq = rng.permutation(N)
+    o3, lse3 = _one_head(orc, q[pq], k, v, 0.4, False)
+    _close(o3, o[pq], 1e-15, "perm Q O")
+    _close(lse3, lse[pq], 1e-15, "perm Q lse")
+    oc, lsec = _one_head(orc, q, k, v, 0.4, True)
+    for i in (0, 1, 5, 17, N - 1):
+        oi, li = _one_head(orc, q[: i + 1], k[: i + 1], v[: i + 1], 0.4, False)
+        _close(oc[i], oi[i], 1e-15, f"causal prefix row {i}")
+        _close(lsec[i], li[i], 1e-15, f"causal prefix lse {i}")
+
+
+def pin_scale_and_linearity(orc):
+    """The scale multiplies q.k: (2q, scale/2) and (4k, scale/4) give identical results
+    (exact powers of two).  O is linear in V."""
+    rng = np.random.default_rng(13)
+    N, d = 29, 6
+    q, k, v, v2 = rng.standard_normal((4, N, d))
+    for causal in (False, True):
+        o, lse = _one_head(orc, q, k, v, 0.3, causal)
+        oa, la = _one_head(orc, 2 * q, k, v, 0.15, causal)
+        ob, lb = _one_head(orc, q, 4 * k, v, 0.075, causal)
+        _close(oa, o, 1e-15, "2q")
+        _close(la, lse, 1e-15, "2q lse")
+        _close(ob, o, 1e-15, "4k")
+        _close(lb, lse, 1e-15, "4k lse")
+        o2, _ = _one_head(orc, q, k, v2, 0.3, causal)
+        o3, _ = _one_head(orc, q, k, 1.5 * v - 0.25 * v2, 0.3, causal)
+        _close(o3, 1.5 * o - 0.25 * o2, 1e-13, "linear in V")
+        # doubling the scale is not the same as doubling V: the weights sharpen
+        o4, _ = _one_head(orc, q, k, v, 0.6, causal)
+        assert np.max(np.abs(o4 - o)) > 1e-3
+
+
+def pin_torch_sdpa(orc):
+    """Cross-check with torch's own CPU fp64 SDPA math path and torch.logsumexp, an
+    independent decomposition of the same operation ([PT] math backend)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(17)
+    for (B, H, N, d) in [(1, 1, 1, 1), (2, 3, 7, 16), (1, 2, 64, 64), (1, 1, 130, 128)]:
+        for causal in (False, True):
+            q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+            scale = 1.0 / math.sqrt(d)
+            o, lse = orc.attn_fwd(q, k, v, scale, causal)
+            tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+            s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+            if causal:
+                s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+            _close(o, ref.numpy(), 1e-12, f"sdpa O {B,H,N,d,causal}")
+            _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, f"sdpa lse {B,H,N,d,causal}")
+
+
+def pin_rows_api(orc):
+    """Row-by-row evaluation returns exactly the rows of the full evaluation."""
+    rng = np.random.default_rng(4)
+    N, d = 70, 9
+    q, k, v = rng.standard_normal((3, N, d))
+    rows = np.array([0, 1, 33, 69, 5, 5])
+    for causal in (False, True):
+        o, lse = _one_head(orc, q, k, v, 0.25, causal)
+        orow, lrow = orc.attn_rows(q, k, v, 0.25, causal, rows)
+        assert np.array_equal(orow, o[rows]) and np.array_equal(lrow, lse[rows])
+
+
+def pin_heads_independent(orc):
+    """Each (b, h) head is its own problem: a batched call equals per-head calls."""
+    rng = np.random.default_rng(6)
+    B, H, N, d = 2, 3, 19, 4
+    q, k, v = rng.standard_normal((3, B, H, N, d))
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, 0.5, causal)
+        for b in range(B):
+            for h in range(H):
+                oh, lh = _one_head(orc, q[b, h], k[b, h], v[b, h], 0.5, causal)
+                assert np.array_equal(o[b, h], oh) and np.array_equal(lse[b, h], lh)
+
+
+ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -1,0 +1,60 @@
+"""The pins catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one slip into a copy of oracle/attn_oracle.c (a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one mask), builds it into a
+temporary library, and runs the whole pin battery on it: at least one pin must
+fail.  Every planted slip keeps all memory accesses in bounds.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, text in attn_oracle.c, replacement); each text must occur exactly once.
+MUTANTS = [
+    ("mask_drops_diagonal", "for (int64_t j = i + 1; j < N; ++j)\n            s[j] = -INFINITY;",
+     "for (int64_t j = i; j < N; ++j)\n            s[j] = -INFINITY;"),
+    ("mask_upper_triangle", "for (int64_t j = i + 1; j < N; ++j)\n            s[j] = -INFINITY;",
+     "for (int64_t j = 0; j < i; ++j)\n            s[j] = -INFINITY;"),
+    ("scale_dropped", "s[j] = dot * scale;\n    }\n    /* step 3", "s[j] = dot;\n    }\n    /* step 3"),
+    ("scale_divides", "s[j] = dot * scale;\n    }\n    /* step 3", "s[j] = dot / scale;\n    }\n    /* step 3"),
+    ("key_row_index", "const double *k_j = k + j * d;", "const double *k_j = k + j;"),
+    ("query_used_as_key", "dot += q_i[c] * k_j[c];", "dot += q_i[c] * q_i[c] * k_j[c];"),
+    ("dot_drops_last_term", "for (int64_t c = 0; c < d; ++c)\n            dot += q_i[c] * k_j[c];",
+     "for (int64_t c = 0; c + 1 < d; ++c)\n            dot += q_i[c] * k_j[c];"),
+    ("exp_sign_flipped", "s[j] = exp(s[j] - m); /* s now", "s[j] = exp(m - s[j]); /* s now"),
+    ("max_not_subtracted_in_lse", "*lse_i = m + log(l);", "*lse_i = log(l);"),
+    ("lse_log2", "*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
+    ("not_normalised", "const double p = s[j] / l;", "const double p = s[j];"),
+    ("value_row_index", "const double *v_j = v + j * d;", "const double *v_j = v + (N - 1 - j) * d;"),
+    ("value_transposed", "o_i[c] += p * v_j[c];", "o_i[c] += p * v[(c % N) * d + (j % d)];"),
+    ("max_is_min", "if (s[j] > m)\n            m = s[j];\n\n    for", "if (s[j] < m || m == -INFINITY)\n            m = s[j];\n\n    for"),
+    ("sum_skips_first_key", "for (int64_t j = 0; j < N; ++j) {\n        s[j] = exp(s[j] - m);",
+     "for (int64_t j = 0; j < N; ++j) {\n        s[j] = exp(s[j] - m) * (j > 0);"),
+    ("dense_mask_off_by_one", "if (causal && j > i) s[j] = -INFINITY;", "if (causal && j >= i + 2) s[j] = -INFINITY;"),
+    ("dense_not_normalised", "for (int64_t j = 0; j < N; ++j) p[j] /= l;", "for (int64_t j = 0; j < N; ++j) p[j] /= (l + 1e-3);"),
+    ("rows_head_offset", "attention_row(q + i * d, k, v, N, d, scale, causal, i, s,",
+     "attention_row(q + i * d, k, v, N, d, scale, causal, 0, s,"),
+    ("batched_head_offset", "const int64_t base = head * N * d;", "const int64_t base = (head / 2) * N * d;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = os.path.join(tmp_path, f"mutant_{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(src=path, out=os.path.join(tmp_path, f"libmutant_{name}.so"), werror=False)
+    orc = oracle.OracleLib(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, RuntimeError, ValueError) as e:
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert caught, f"no pin caught mutant {name}"
