@@ -1,0 +1,177 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3]
+
+A step is one call of attn_fwd (the whole fused forward: Q tile load, K/V
+staging, both matrix products, online softmax, normalisation, O and lse
+stores) over one batch of seeded synthetic inputs already resident in HBM.
+The default workload is causal bf16 attention with B=2, H=32, N=8192, d=128.
+Prints one JSON line: throughput in TFLOP/s at the algorithmic count
+4*B*H*N^2*d (halved when causal), the kernel's roofline figures, and the fp64
+CPU oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_hbm_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_96_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source and this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if "=" in ln and not ln.lstrip().startswith("#"):
+                k, v = ln.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash() or kv.get("workload") != workload_name:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, budget_heads: int):
+    """The fp64 oracle (as it stands) on whole heads of the same workload."""
+    import oracle
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:budget_heads]
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        oracle.attn_rows(q[b, h], k[b, h], v[b, h], w.scale, w.causal, range(w.N))
+    dt = time.perf_counter() - t0
+    flops = w.flops * len(heads) / (w.B * w.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} heads, all {w.N} query rows each "
+                      f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
+
+
+def copy_probe(nbytes: int, steps: int):
+    """A plain device copy of known size (counter calibration run)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                      "steps": steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", help="c1..c5 (default: c3, the headline)")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the workload the CPU oracle runs for cpu_baseline (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward is not sharded across "
+              "GPUs in this library (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_96_amd as ea
+    from exact_attention_96_amd.workloads import WORKLOADS, make_inputs
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = make_inputs(w)
+    dev = "cuda:0"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        ea.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = w.flops * args.steps / wall / 1e12
+
+    achieved = w.flops / avg_kernel_s / 1e12
+    peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_MFMA_BF16_TFLOPS
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16 causal, N=8192 d=128) and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded randn inputs, see exact_attention_96_amd/workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "algorithmic_bytes": w.io_bytes,
+                     "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
+                     "kernel_source_sha": kernel_source_hash()},
+    }
+    if args.cpu_heads > 0:
+        print(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

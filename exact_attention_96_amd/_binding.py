@@ -1,0 +1,115 @@
+"""ctypes binding of libattn.so (argument marshalling only).
+
+Every step of the forward runs in the HIP library; this module checks the
+tensors, allocates the outputs with torch and passes raw device pointers and
+torch's current HIP stream to ``attn_fwd`` (declared in include/attn.h).
+There is no fallback: a missing library or a failed call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn_fwd failed: status {status} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library not built: {LIB_PATH} is missing "
+                "(run `python -m exact_attention_96_amd.build`)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        ci = ctypes.c_int
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
+        L.attn_fwd.restype = ci
+        L.attn_strerror.argtypes = [ci]
+        L.attn_strerror.restype = ctypes.c_char_p
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().attn_abi_version())
+
+
+def attn_fwd_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+                 scale: float, causal: int, dtype: int, stream: int) -> int:
+    """Raw call with integer device addresses; returns the status code."""
+    return int(lib().attn_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
+                              causal, dtype, stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Attention forward on the GPU.
+
+    q, k, v: torch tensors [B, H, N, d] on one HIP device, same dtype
+    (float32, float16 or bfloat16), contiguous.  Returns (o, lse): o like q,
+    lse float32 [B, H, N] with lse = ln sum_j e^{s_ij}.  ``scale`` defaults to
+    1/sqrt(d) rounded to fp32.  The call is enqueued on torch's current stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    code = _dtype_code(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), int(bool(causal)), code, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, strerror(st))
+    return out, lse

@@ -1,0 +1,109 @@
+// C ABI of the attention library: argument checks, kernel selection, launch.
+// The operation and every argument are specified in include/attn.h.
+#include "attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fwd_f32.hpp"
+#include "fwd_mfma.hpp"
+
+namespace {
+
+using attn::FwdArgs;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Half-open byte ranges [p, p + n) and [r, r + m) intersect.
+bool overlaps(const void *p, uint64_t n, const void *r, uint64_t m) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(r);
+    return a0 < b0 + m && b0 < a0 + n;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const FwdArgs &a, int bh, hipStream_t stream) {
+    constexpr int QW = attn::F32Fwd<D, CAUSAL>::QW;
+    FwdArgs b = a;
+    b.n_qtiles = (a.N + QW - 1) / QW;
+    b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
+    hipLaunchKernelGGL((attn::attn_fwd_f32_kernel<D, CAUSAL>), dim3(b.total),
+                       dim3(attn::F32Fwd<D, CAUSAL>::THREADS), 0, stream, b);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
+    typedef attn::MfmaFwd<T, D, CAUSAL> K;
+    FwdArgs b = a;
+    b.n_qtiles = (a.N + K::BR - 1) / K::BR;
+    b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
+    hipLaunchKernelGGL((attn::attn_fwd_mfma_kernel<T, D, CAUSAL>), dim3(b.total), dim3(K::THREADS), 0,
+                       stream, b);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t dispatch_dtype(const FwdArgs &a, int bh, int dtype, hipStream_t stream) {
+    switch (dtype) {
+        case ATTN_F32: return launch_f32<D, CAUSAL>(a, bh, stream);
+        case ATTN_F16: return launch_mfma<_Float16, D, CAUSAL>(a, bh, stream);
+        default: return launch_mfma<__bf16, D, CAUSAL>(a, bh, stream);
+    }
+}
+
+template <int D>
+hipError_t dispatch_causal(const FwdArgs &a, int bh, int causal, int dtype, hipStream_t stream) {
+    return causal ? dispatch_dtype<D, true>(a, bh, dtype, stream)
+                  : dispatch_dtype<D, false>(a, bh, dtype, stream);
+}
+
+}  // namespace
+
+extern "C" ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                        int N, int d, float scale, int causal, int dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!isfinite(scale)) return ATTN_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return ATTN_EINVAL;
+    const uint64_t elt = dtype == ATTN_F32 ? 4 : 2;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t tbytes = rows * (uint64_t)d * elt;
+    const uint64_t lbytes = rows * 4;
+    if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) || overlaps(o, tbytes, v, tbytes) ||
+        overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
+        overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes))
+        return ATTN_EINVAL;
+    if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+    // the smallest query tile is 32 rows; the 1-D grid holds at most INT32_MAX workgroups
+    if ((uint64_t)B * (uint64_t)H * (((uint64_t)N + 31) / 32) > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
+
+    FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.N = N;
+    a.n_qtiles = 0;
+    a.total = 0;
+    a.c = (float)((double)scale * 1.4426950408889634073599);
+    const int bh = B * H;
+    const hipError_t err = d == 64 ? dispatch_causal<64>(a, bh, causal, dtype, stream)
+                                   : dispatch_causal<128>(a, bh, causal, dtype, stream);
+    return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" ATTN_API const char *attn_strerror(int status) {
+    switch (status) {
+        case ATTN_OK: return "success";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension or problem size";
+        case ATTN_EHIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" ATTN_API int attn_abi_version(void) { return ATTN_ABI_VERSION; }

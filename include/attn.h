@@ -1,0 +1,106 @@
+/*
+ * attn.h — C ABI of the exact attention forward library for MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention, one (batch, head) at a
+ * time:
+ *
+ *   S = scale * Q K^T,   S_ij = -inf where causal and key j > query i,
+ *   P = softmax(S) over the key axis,   O = P V,
+ *   lse_i = log sum_j e^{S_ij} = m_i + log l_i   (natural log)
+ *
+ * as defined in "Understand FlashAttention" (nothiny.github.io), section
+ * "Attention 前向和反向传播公式 / 前向传播" (S = Q K^T, P = softmax(S), O = P V)
+ * and its appendix "附：数值稳定的logsumexp(L)推导" (L = m + log l), with the
+ * scale and the lower-triangle causal mask of "PyTorch profiling part 3:
+ * attention" (Hugging Face blog), sections "朴素注意力" and "构建因果掩码".
+ * It is computed FlashAttention-style ("Understand FlashAttention", section
+ * "FlashAttention": Q split into row blocks in the outer loop, K/V into column
+ * blocks in the inner loop; section "两块情况的完整推导": running row max m and
+ * normaliser l, the partial output rescaled by e^{m_old - m_new}), so the
+ * N x N score matrix never reaches device memory.
+ *
+ * All entry points are extern "C" and take plain pointers and sizes.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of this header are the library's only exported names. */
+#define ATTN_API __attribute__((visibility("default")))
+
+/* Element type of q, k, v and o.  lse is always fp32. */
+typedef enum {
+    ATTN_F32 = 0,  /* IEEE binary32 */
+    ATTN_F16 = 1,  /* IEEE binary16 */
+    ATTN_BF16 = 2  /* bfloat16 */
+} attn_dtype_t;
+
+/* Return codes. */
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,       /* invalid argument; nothing was launched */
+    ATTN_EUNSUPPORTED = 2, /* valid but unsupported (head dim, size); nothing launched */
+    ATTN_EHIP = 3          /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+/* Version of this ABI; bumped on any incompatible change. */
+#define ATTN_ABI_VERSION 1
+
+/*
+ * attn_fwd — attention forward for B*H independent heads.
+ *
+ * Arguments
+ *   q, k, v  device pointers, each [B, H, N, d] contiguous, d innermost, of
+ *            element type `dtype`; read only.
+ *   o        device pointer, [B, H, N, d] contiguous of `dtype`; written.
+ *            o[b,h,i,:] = sum_j P_ij v[b,h,j,:], rounded to `dtype` (nearest even).
+ *   lse      device pointer, [B, H, N] contiguous fp32; written.
+ *            lse[b,h,i] = m_i + ln l_i of the scaled, masked score row.
+ *   B, H, N  batch, heads, sequence length (queries and keys alike), each >= 1.
+ *   d        head dimension; 64 or 128.
+ *   scale    finite multiplier of q.k (the usual value is 1/sqrt(d)).
+ *   causal   0: every key is visible; 1: key j is visible to query i iff j <= i.
+ *   dtype    an attn_dtype_t.
+ *   stream   HIP stream the work is enqueued on (0 = the null stream).
+ *
+ * Arithmetic: bf16/fp16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; the softmax statistics and the output accumulator are fp32;
+ * the probabilities fed to the second product are rounded to the input type.
+ * fp32 inputs are processed entirely in fp32.  Results of one build on one
+ * input are bitwise reproducible from call to call.
+ *
+ * Ownership and concurrency: all buffers belong to the caller.  The library
+ * allocates no memory and keeps no mutable state, so calls on different
+ * streams or host threads may run concurrently.  o and lse must not overlap
+ * q, k, v or each other.
+ *
+ * Errors are returned synchronously and nothing is launched on error:
+ *   ATTN_EINVAL       a NULL pointer; B, H or N < 1; d < 1; unknown dtype;
+ *                     causal not 0/1; non-finite scale; q, k, v or o not 16-byte
+ *                     aligned or lse not 4-byte aligned; o or lse overlapping
+ *                     q, k, v or each other.
+ *   ATTN_EUNSUPPORTED d not 64 or 128; a problem whose tile count exceeds the
+ *                     launch grid.
+ *   ATTN_EHIP         the launch failed (hipGetLastError).
+ * The call is asynchronous: results are valid once `stream` has completed.
+ */
+ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+ATTN_API const char *attn_strerror(int status);
+
+/* Returns ATTN_ABI_VERSION of the built library. */
+ATTN_API int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

@@ -1,0 +1,89 @@
+"""The C-ABI library: loads, exports what include/attn.h declares, rejects bad
+arguments before touching the GPU (CPU only: no compute call is made)."""
+import os
+import re
+
+import pytest
+
+import exact_attention_96_amd as ea
+from exact_attention_96_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]*?\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == ["attn_abi_version", "attn_fwd", "attn_strerror"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _binding.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), f"{name} not exported by {_binding.LIB_PATH}"
+
+
+def test_library_exports_nothing_else():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln})
+    assert funcs == declared_symbols()
+
+
+def test_abi_version_matches_header():
+    with open(HEADER) as f:
+        m = re.search(r"#define ATTN_ABI_VERSION (\d+)", f.read())
+    assert ea.abi_version() == int(m.group(1))
+
+
+def test_strerror():
+    assert ea.strerror(0) == "success"
+    assert "invalid" in ea.strerror(1)
+    assert "unsupported" in ea.strerror(2)
+    assert "HIP" in ea.strerror(3)
+    assert ea.strerror(12345) == "unknown status"
+
+
+# Fake, well separated, 16-byte aligned addresses: every case below is rejected by
+# the host checks, which run before any HIP call.
+Q, K, V, O, L = (i << 40 for i in range(1, 6))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, scale=0.125, causal=1, dtype=2,
+            stream=0)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return ea.attn_fwd_ptr(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                           a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+    dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1), dict(N=-5),
+    dict(dtype=3), dict(dtype=-1), dict(causal=2), dict(causal=-1),
+    dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(q=Q + 8), dict(k=K + 2), dict(v=V + 4), dict(o=O + 8), dict(lse=L + 2),
+    dict(o=Q), dict(o=K + 16), dict(o=V + 1600), dict(lse=Q + 64), dict(lse=O + 4),
+    dict(o=Q - 16),  # o ends inside q
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_invalid_arguments(kw):
+    assert call(**kw) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(d=256), dict(d=65),
+                                dict(B=65536, H=65536, N=1, d=64)])
+def test_unsupported(kw):
+    assert call(**kw) == ea.ATTN_EUNSUPPORTED
+
+
+def test_lse_just_after_o_is_fine_to_check():
+    # o occupies B*H*N*d*2 bytes; lse placed right after it does not overlap o.
+    nbytes = 2 * 3 * 100 * 64 * 2
+    assert call(dtype=7, lse=O + nbytes) == ea.ATTN_EINVAL  # rejected for the dtype only

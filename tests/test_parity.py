@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generators in exact_attention_96_amd.workloads and
+go unchanged to both sides; the oracle reads the very values the GPU sees,
+widened exactly to fp64.  Bars are in parity_util.TOL.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_96_amd as ea
+import oracle
+from exact_attention_96_amd.workloads import WORKLOADS, make_inputs, random_qkv
+from parity_util import check, errors, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need an MI355X"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), f"built for gfx950, found {name}"
+
+
+def run_gpu(q, k, v, causal, scale):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o, lse = ea.attn_fwd(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def full_parity(q, k, v, causal, scale, dtype, what):
+    say(f"[parity] {what}: shape={tuple(q.shape)} dtype={dtype} causal={causal} scale={scale}")
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, causal)
+    err = errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    check(err, dtype, what)
+    return o, lse, err
+
+
+# ------------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c4"])
+def test_workload_full(key):
+    """Small and medium workloads, every output element against the oracle."""
+    w = WORKLOADS[key]
+    q, k, v = make_inputs(w)
+    full_parity(q, k, v, w.causal, w.scale, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("key", ["c3", "c5"])
+def test_workload_sampled(key):
+    """Full-size workloads in the benchmark's launch configuration: sampled rows of
+    three heads against the oracle row by row, plus properties of every row."""
+    w = WORKLOADS[key]
+    q, k, v = make_inputs(w)
+    say(f"[parity] {w.name}: full-size launch, shape={tuple(q.shape)}")
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    o_c, lse_c = o.float().cpu(), lse.cpu()
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    for (b, h) in heads:
+        rows = sample_rows(w.N, rng)
+        o_ref, lse_ref = oracle.attn_rows(q[b, h], k[b, h], v[b, h], w.scale, w.causal, rows)
+        err = errors(o_c[b, h, rows].numpy(), lse_c[b, h, rows].numpy(), o_ref, lse_ref)
+        check(err, w.dtype, f"{w.name} head ({b},{h}) rows {len(rows)}")
+    # properties of every row: finite; each output is a convex combination of V rows
+    assert torch.isfinite(o_c).all() and torch.isfinite(lse_c).all()
+    vf = v.float()
+    assert (o_c <= vf.amax(dim=2, keepdim=True) + 1e-2).all()
+    assert (o_c >= vf.amin(dim=2, keepdim=True) - 1e-2).all()
+    if w.causal:  # row 0 sees key 0 alone: o_0 = v_0 exactly, lse_0 = s_00
+        assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+        s00 = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) * w.scale
+        assert (lse_c[:, :, 0].double() - s00).abs().max() <= 1e-4
+
+
+# ------------------------------------------------------------------ shapes
+
+ODD_N = [1, 2, 3, 31, 33, 63, 65, 127, 129, 200, 385, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(dtype, d, causal):
+    """Lengths that are not tile multiples (tails of 1..127 rows), several heads."""
+    for i, N in enumerate(ODD_N):
+        q, k, v = random_qkv(2, 3, N, d, dtype, seed=100 + i)
+        full_parity(q, k, v, causal, 1.0 / math.sqrt(d), dtype, f"ragged N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_many_heads_short(dtype):
+    q, k, v = random_qkv(8, 40, 96, 64, dtype, seed=7)
+    full_parity(q, k, v, True, 0.125, dtype, "B=8 H=40 N=96")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scale_values(dtype):
+    """scale = 0 (uniform weights), negative, and large (sharp softmax)."""
+    q, k, v = random_qkv(1, 2, 200, 64, dtype, seed=9)
+    for scale in (0.0, -0.2, 1.0):
+        for causal in (False, True):
+            full_parity(q, k, v, causal, scale, dtype, f"scale={scale}")
+
+
+# ------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_constant_v_and_zero_q(dtype):
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = random_qkv(B, H, N, d, dtype, seed=21)
+    c = torch.randn(d).to(v.dtype)
+    vc = c.expand(B, H, N, d).contiguous()
+    say(f"[invariant] constant V dtype={dtype}")
+    o, _ = run_gpu(q, k, vc, True, 1.0 / math.sqrt(d))
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert (o.float().cpu() - c.float()).abs().max() <= tol
+    say(f"[invariant] zero Q dtype={dtype}")
+    qz = torch.zeros_like(q)
+    o, lse = run_gpu(qz, k, v, True, 0.125)
+    mean = v.double().cumsum(dim=2) / torch.arange(1, N + 1, dtype=torch.float64)[:, None]
+    assert (o.double().cpu() - mean).abs().max() <= tol
+    assert (lse.double().cpu() - torch.log(torch.arange(1, N + 1, dtype=torch.float64))).abs().max() <= 1e-3
+
+
+def test_deterministic():
+    w = WORKLOADS["c2"]
+    q, k, v = (t.to(DEV) for t in make_inputs(w))
+    say("[determinism] c2 twice")
+    o1, l1 = ea.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    o2, l2 = ea.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_guard_bands_untouched():
+    """Outputs written into the middle of larger buffers: nothing outside is touched."""
+    B, H, N, d = 2, 2, 333, 64
+    q, k, v = (t.to(DEV) for t in random_qkv(B, H, N, d, "bf16", seed=5))
+    pad = 4096
+    n_o, n_l = B * H * N * d, B * H * N
+    obuf = torch.full((n_o + 2 * pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((n_l + 2 * pad,), -3.0, dtype=torch.float32, device=DEV)
+    o = obuf[pad:pad + n_o].view(B, H, N, d)
+    lse = lbuf[pad:pad + n_l].view(B, H, N)
+    say("[guard] bf16 N=333 into padded buffers")
+    ea.attn_fwd(q, k, v, causal=True, scale=0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (obuf[:pad] == 7.0).all() and (obuf[pad + n_o:] == 7.0).all()
+    assert (lbuf[:pad] == -3.0).all() and (lbuf[pad + n_l:] == -3.0).all()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, 0.125, True)
+    check(errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "bf16", "guard")
+
+
+def test_side_stream():
+    q, k, v = (t.to(DEV) for t in random_qkv(1, 4, 257, 128, "f16", seed=3))
+    s = torch.cuda.Stream()
+    say("[stream] f16 on a side stream")
+    with torch.cuda.stream(s):
+        o, lse = ea.attn_fwd(q, k, v, causal=False, scale=0.0884)
+    s.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, 0.0884, False)
+    check(errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "f16", "stream")
+
+
+def test_binding_rejects_bad_tensors():
+    q = torch.zeros(1, 1, 8, 64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ea.attn_fwd(q, q, q.half())
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, q, q[..., :32])
+    with pytest.raises(ea.AttnError) as e:
+        z = torch.zeros(1, 1, 8, 96, device=DEV, dtype=torch.bfloat16)
+        ea.attn_fwd(z, z, z)
+    assert e.value.status == ea.ATTN_EUNSUPPORTED
