@@ -37,8 +37,14 @@ hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
     FwdArgs b = a;
     b.n_qtiles = (a.N + K::BR - 1) / K::BR;
     b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
-    hipLaunchKernelGGL((attn::attn_fwd_mfma_kernel<T, D, CAUSAL>), dim3(b.total), dim3(K::THREADS), 0,
-                       stream, b);
+    constexpr int lds_bytes = 2 * K::STAGE_B;
+    // opt in to the LDS size once per kernel (thread-safe static initialisation)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((attn::attn_fwd_mfma_kernel<T, D, CAUSAL>), dim3(b.total), dim3(K::THREADS),
+                       lds_bytes, stream, b);
     return hipGetLastError();
 }
 

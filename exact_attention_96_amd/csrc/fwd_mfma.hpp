@@ -1,27 +1,42 @@
 // Fused attention forward on the gfx950 matrix cores (bf16 / fp16 inputs).
 //
-// One workgroup owns one (batch*head, query tile) pair: BR = 128 query rows,
-// 32 per wave, the outer loop of "Understand FlashAttention", section
-// "FlashAttention".  The inner loop walks the key/value sequence in BC = 64
-// column blocks staged in LDS.  Per block, each wave applies the update of
-// that page's section "两块情况的完整推导" (steps 5-7): new row max, rescale
-// factor e^{m_old - m_new}, row sum, rescaled partial output plus P V; after
-// the last block it divides by the row sum (step 8) and writes
-// lse = m + log l (appendix "附：数值稳定的logsumexp(L)推导").
+// Decomposition ("Understand FlashAttention", section "FlashAttention": outer
+// loop over row blocks of Q, inner loop over column blocks of K and V).  One
+// workgroup owns one (batch*head, query tile) pair of BR = 256 query rows;
+// each of its 4 waves (one per SIMD) owns 64 rows as two groups of 32.  The
+// inner loop walks keys in tiles of BC = 64, and per tile every wave applies
+// the update of that page's section "两块情况的完整推导" (steps 5-7): row max,
+// rescale of the running sum and of the unnormalised output, P V; after the
+// last tile it divides by the row sum (step 8) and writes the row
+// log-sum-exp (appendix "附：数值稳定的logsumexp(L)推导").
 //
-// Layout trick.  The first product is evaluated transposed, S^T = K Q^T, with
-// the 32x32x16 MFMA: its accumulator gives every lane one query (lane % 32)
-// and 16 keys, so the row max and row sum are in-lane reductions plus one
-// exchange with lane ^ 32.  Keys are fed to the A operand in the order
-// sigma(r) = r with bits 2 and 3 swapped; then the 8 accumulator registers
-// i = 8h .. 8h+7 of lane group g hold the 8 consecutive keys 16h + 8g .. +7,
-// which is exactly the B-operand layout the second product O^T = V^T P^T
-// needs.  P therefore goes from the softmax straight into the MFMA, and the
-// per-query rescale of O^T is a per-lane multiply.  V is stored transposed in
-// LDS (d rows of keys) so its A-operand fragments are 16-byte reads.
+// Data movement.  K and V tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging), double buffered: the loads
+// of tile j+1 are in flight while tile j is computed, with one barrier per
+// tile.  Both tiles keep their row-major layout, each 16-byte chunk of a row
+// placed at chunk index XOR a row-dependent swizzle so that every fragment
+// read below is free of LDS bank conflicts.
 //
-// The exponentials use exp2 with the scale folded into log2(e): t = s * c,
-// c = scale * log2(e), p = 2^{t - m}.
+// First product, transposed: S^T = K Q^T with v_mfma_f32_32x32x16.  Q^T is the
+// B operand, held in registers for the whole loop.  Its accumulator gives
+// every lane one query row (lane % 32) and 16 keys, so row max and row sum
+// are in-lane reductions plus one exchange with lane ^ 32 (permlane32 swap).
+// The K rows of each 32-key block are stored in the order sigma(r) = r with
+// bits 2 and 3 swapped; then accumulator registers 8h .. 8h+7 of lane half g
+// hold the consecutive keys 16h + 8g .. 16h + 8g + 7, which is exactly the B
+// operand layout of the second product O^T = V^T P^T: P goes from the softmax
+// to the matrix core without leaving registers, and the per-row rescale of O^T
+// is a per-lane multiply.  The V^T A operand comes from the row-major V tile
+// through ds_read_b64_tr_b16 (each 16-lane group transposes a 4 x 16 block).
+//
+// Softmax arithmetic.  t = s * c with c = scale * log2(e); p = 2^(t - m).
+// The reference m is only moved when a tile's row max exceeds it by more than
+// TAU = 8 (in log2 units), so the O rescale runs a handful of times per row
+// instead of once per tile.  This changes no result: softmax is invariant to
+// the shift (same page, "数值稳定的 Softmax"), and p <= 2^8 keeps every
+// intermediate far inside fp32/bf16/fp16 range.  The row sum adds the fp32
+// probabilities before their rounding to the input type, so lse keeps fp32
+// accuracy (a sum of bf16-rounded terms would cost ~2^-9 relative in l).
 #pragma once
 
 #include "common.hpp"
@@ -38,21 +53,37 @@ struct FwdArgs {
     float c;         // scale * log2(e)
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
 template <typename T> struct Mfma;
 
 template <> struct Mfma<__bf16> {
     typedef bf16x8_t v8;
     typedef bf16x4_t v4;
+    typedef bf16x2_t v2;
     static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // round a pair to bf16 (nearest even), packed low | high << 16
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        const f32x2_t v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2));
     }
 };
 
 template <> struct Mfma<_Float16> {
     typedef f16x8_t v8;
     typedef f16x4_t v4;
+    typedef f16x2_t v2;
     static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        const f32x2_t v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2));
     }
 };
 
@@ -61,193 +92,331 @@ __device__ __forceinline__ int swap_bits23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ float lane_swap32_max(float x) {
+    // v_permlane32_swap: returns (x of lanes 0..31 in both halves, x of lanes 32..63 in both halves)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_swap32_add(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+template <typename T, int D, bool CAUSAL, int QG = 1>
 struct MfmaFwd {
-    static constexpr int NW = 4;           // waves per workgroup
-    static constexpr int QW = 32;          // query rows per wave
-    static constexpr int BR = NW * QW;     // query rows per workgroup
-    static constexpr int BC = 64;          // keys per inner iteration
+    static constexpr int NW = 8 / QG;          // waves per workgroup
+    static constexpr int QW = 32 * QG;         // query rows per wave (QG groups of 32)
+    static constexpr int BR = NW * QW;         // query rows per workgroup (256)
+    static constexpr int BC = 64;              // keys per tile
     static constexpr int THREADS = NW * 64;
-    static constexpr int KSTRIDE = D + 8;  // K tile row pitch (elements): 16 B pad, conflict-free
-    static constexpr int VSTRIDE = BC + 8; // V^T tile row pitch (elements)
-    static constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    static constexpr int DC = D / 16;      // 16-deep d chunks of the first product
-    typedef typename Mfma<T>::v8 v8;
-    typedef typename Mfma<T>::v4 v4;
+    static constexpr int CH = D / 8;           // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;         // bytes per K/V row
+    static constexpr int TILE_B = BC * ROWB;   // bytes per K or V tile
+    static constexpr int STAGE_B = 2 * TILE_B; // K tile then V tile
+    static constexpr int LOADS = BC * CH / 64 / NW;  // 16-byte-per-lane loads per wave per tile
+    static constexpr int DB = D / 32;          // 32-row blocks of O^T
+    static constexpr int DC = D / 16;          // k-steps of the first product
+    static constexpr int KC = BC / 16;         // k-steps of the second product
+    static constexpr float TAU = 8.0f;
+    typedef Mfma<T> M;
+    typedef typename M::v8 v8;
+
+    // chunk swizzles (see the bank analysis in the header comment of this file)
+    static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
     static __device__ __forceinline__ v8 as_v8(u32x4_t x) { return __builtin_bit_cast(v8, x); }
 
-    static __device__ void run(const FwdArgs &a) {
-        __shared__ __attribute__((aligned(16))) uint16_t k_lds[BC * KSTRIDE];
-        __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTRIDE];
+    // State a wave carries across key tiles.
+    struct State {
+        v8 qf[QG][DC];           // Q^T fragments of the wave's row groups
+        f32x16_t acc[QG][DB];    // unnormalised O^T
+        float m_ref[QG];         // reference row max (log2 domain)
+        float lsum[QG];          // this lane's share of the row sums
+        uint32_t kfrag;          // LDS byte offset of K fragment k-step 0 (k-step cc: ^ cc << 5)
+        uint32_t vfrag;          // LDS byte offset of V^T fragment block 0 (block db: ^ db << 6)
+    };
 
-        const int N = a.N;
-        const int logical = xcd_contiguous(blockIdx.x, a.total);
-        const int bh = logical / a.n_qtiles;
-        const int t = logical - bh * a.n_qtiles;
-        // causal: the longest rows first, so the short ones fill the tail of the grid
-        const int qt = CAUSAL ? a.n_qtiles - 1 - t : t;
-        const size_t head = (size_t)bh * (size_t)N * D;
-        const uint16_t *Qh = static_cast<const uint16_t *>(a.q) + head;
-        const uint16_t *Kh = static_cast<const uint16_t *>(a.k) + head;
-        const uint16_t *Vh = static_cast<const uint16_t *>(a.v) + head;
-
-        const int tid = threadIdx.x;
-        const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-        const int q0 = qt * BR + w * QW;      // first query row of this wave
-        const int qrow = q0 + l32;            // this lane's query row
-
-        // Q^T as the B operand: lane holds Q[qrow][16c + 8g .. +7] for every chunk c.
-        v8 qf[DC];
+    // One key tile for one wave.  MASKED: the tile crosses the diagonal or the
+    // end of the sequence, so scores of invisible keys are dropped.
+    template <bool MASKED>
+    static __device__ __forceinline__ void tile(State &S, uint32_t st, int k0, int q0, int N,
+                                                float c, int l32, int g) {
+        const uint32_t kbase = S.kfrag + st, vbase = S.vfrag + st;
+        // ---- S^T = K Q^T: two 32-key blocks x QG 32-row groups
+        f32x16_t s[QG][2];
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (qrow < N) x = *reinterpret_cast<const u32x4_t *>(Qh + (size_t)qrow * D + c * 16 + g * 8);
-            qf[c] = as_v8(x);
-        }
-
-        f32x16_t acc[DB];
+        for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
-        float m = -INFINITY;  // running max of t = s * c (log2 domain)
-        float lsum = 0.f;     // this lane's share of the running row sum
-
-        const int n_kv_all = (N + BC - 1) / BC;
-        const int n_kv = CAUSAL ? min(n_kv_all, (qt * BR + BR - 1) / BC + 1) : n_kv_all;
-
-        for (int j = 0; j < n_kv; ++j) {
-            const int k0 = j * BC;
-            __syncthreads();  // every wave is done with the previous tile
-            // K tile -> LDS, rows permuted by sigma inside each 32-row block.
-            for (int idx = tid; idx < BC * D / 8; idx += THREADS) {
-                const int r = idx / (D / 8), cc = idx % (D / 8);
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (k0 + r < N) x = *reinterpret_cast<const u32x4_t *>(Kh + (size_t)(k0 + r) * D + cc * 8);
-                const int rr = (r & ~31) | swap_bits23(r & 31);
-                *reinterpret_cast<u32x4_t *>(k_lds + rr * KSTRIDE + cc * 8) = x;
-            }
-            // V tile -> LDS transposed: vt[d][key].  Lane pairs up keys 2*l32, 2*l32+1.
-            for (int cc = w * 2 + g; cc < D / 8; cc += 2 * NW) {
-                const int r0 = 2 * l32;
-                u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-                if (k0 + r0 < N) x0 = *reinterpret_cast<const u32x4_t *>(Vh + (size_t)(k0 + r0) * D + cc * 8);
-                if (k0 + r0 + 1 < N) x1 = *reinterpret_cast<const u32x4_t *>(Vh + (size_t)(k0 + r0 + 1) * D + cc * 8);
+                for (int i = 0; i < 16; ++i) s[qg][kb][i] = 0.f;
+        // all K fragments of the tile are requested before the first MFMA
+        v8 kf[2][DC];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = (x0[e] & 0xffffu) | (x1[e] << 16);
-                    const uint32_t hi = (x0[e] >> 16) | (x1[e] & 0xffff0000u);
-                    *reinterpret_cast<uint32_t *>(vt_lds + (cc * 8 + 2 * e) * VSTRIDE + r0) = lo;
-                    *reinterpret_cast<uint32_t *>(vt_lds + (cc * 8 + 2 * e + 1) * VSTRIDE + r0) = hi;
-                }
-            }
-            __syncthreads();
-
-            if (CAUSAL && k0 > q0 + QW - 1) continue;  // every key of the tile is after every row
-
-            // S^T = K Q^T for the two 32-key blocks of the tile.
-            f32x16_t s[2];
-            bool on[2];
+        for (int cc = 0; cc < DC; ++cc)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                on[kb] = (k0 + kb * 32 < N) && (!CAUSAL || k0 + kb * 32 <= q0 + QW - 1);
+            for (int kb = 0; kb < 2; ++kb)
+                kf[kb][cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)((kbase ^ (cc << 5)) + kb * 32 * ROWB));
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-                if (on[kb]) {
+        for (int cc = 0; cc < DC; ++cc)
 #pragma unroll
-                    for (int c = 0; c < DC; ++c) {
-                        const v8 kf = as_v8(*reinterpret_cast<const u32x4_t *>(
-                            k_lds + (kb * 32 + l32) * KSTRIDE + c * 16 + g * 8));
-                        s[kb] = Mfma<T>::mma(kf, qf[c], s[kb]);
-                    }
-                }
-            }
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) s[qg][kb] = M::mma(kf[kb][cc], S.qf[qg][cc], s[qg][kb]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DC, 0);      // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DC * QG, 0); // then the MFMAs
 
-            // Scale to the log2 domain and mask.  Register i of block kb is key
-            // k0 + 32 kb + (i & 7) + 8 g + 16 (i >> 3).
-            const bool need_mask = (CAUSAL && k0 + BC - 1 > q0) || (k0 + BC > N);
+        // ---- visibility of register i of block kb: key k0 + 32 kb + (i & 7) + 8 g + 16 (i >> 3)
+        auto visible = [&](int qg, int kb, int i) {
+            const int key = k0 + 32 * kb + (i & 7) + 8 * g + 16 * (i >> 3);
+            const int q = q0 + 32 * qg + l32;
+            return key < N && (!CAUSAL || key <= q);
+        };
+
+        // ---- row max per group
+        float mt[QG];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
             float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = s[kb][i] * a.c;
-                    if (need_mask) {
-                        const int key = k0 + kb * 32 + (i & 7) + 8 * g + 16 * (i >> 3);
-                        const bool dead = !on[kb] || key >= N || (CAUSAL && key > qrow);
-                        x = dead ? -INFINITY : x;
-                    } else if (!on[kb]) {
-                        x = -INFINITY;
-                    }
-                    s[kb][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a row with no key yet
-            const float alpha = fast_exp2(m - m_use);
-            m = m_new;
-
-            float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(s[kb][i] - m_use);
-                    s[kb][i] = p;
-                    rs += p;
+                    const float x = s[qg][kb][i];
+                    mx = fmaxf(mx, MASKED ? (visible(qg, kb, i) ? x : -INFINITY) : x);
                 }
-            lsum = lsum * alpha + rs;
+            mx = lane_swap32_max(mx);
+            mt[qg] = MASKED ? (mx == -INFINITY ? -INFINITY : mx * c) : mx * c;
+        }
+        // ---- move the reference max only when a row max outgrows it by TAU
+        bool grow = false;
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+        for (int qg = 0; qg < QG; ++qg) grow = grow || (mt[qg] > S.m_ref[qg] + TAU);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
-
-            // O^T += V^T P^T, 16 keys per MFMA.
+            for (int qg = 0; qg < QG; ++qg) {
+                const float m_new = fmaxf(S.m_ref[qg], mt[qg]);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref[qg] - m_new);
+                S.lsum[qg] *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (!on[kb]) continue;
+                for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    v8 pf;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(s[kb][8 * h + e]);
-#pragma unroll
-                    for (int b = 0; b < DB; ++b) {
-                        const v8 vf = as_v8(*reinterpret_cast<const u32x4_t *>(
-                            vt_lds + (b * 32 + l32) * VSTRIDE + kb * 32 + 16 * h + 8 * g));
-                        acc[b] = Mfma<T>::mma(vf, pf, acc[b]);
-                    }
-                }
+                    for (int i = 0; i < 16; ++i) S.acc[qg][b][i] *= alpha;
+                S.m_ref[qg] = m_new;
             }
         }
 
-        // Epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
-        // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row qrow.
-        const float ltot = lsum + __shfl_xor(lsum, 32);
-        if (qrow < N) {
-            const float inv = 1.f / ltot;
-            uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)qrow * D;
+        // ---- V^T fragments requested now; their latency hides behind the exponentials
+        v8 vf[KC][DB];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint32_t vb = (vbase ^ (db << 6)) + kc * 16 * ROWB;
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb + 4 * ROWB));
+                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                vf[kc][db] = as_v8((u32x4_t){l2[0], l2[1], h2[0], h2[1]});
+            }
+
+        // ---- P = 2^(s c - m), rounded to T in pairs; row sums from the rounded pairs
+        uint32_t pk[QG][KC][4];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            const float nm = S.m_ref[qg] == -INFINITY ? 0.f : -S.m_ref[qg];
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i0 = 8 * h + 2 * e;
+                        float p0 = fast_exp2(fmaf(s[qg][kb][i0], c, nm));
+                        float p1 = fast_exp2(fmaf(s[qg][kb][i0 + 1], c, nm));
+                        if (MASKED) {
+                            p0 = visible(qg, kb, i0) ? p0 : 0.f;
+                            p1 = visible(qg, kb, i0 + 1) ? p1 : 0.f;
+                        }
+                        pk[qg][2 * kb + h][e] = M::pack(p0, p1);
+                        rs += p0 + p1;
+                    }
+            S.lsum[qg] += rs;
+        }
+
+        // ---- O^T += V^T P^T, 16 keys per MFMA; each V fragment serves every row group
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) {
+                    const u32x4_t pp = {pk[qg][kc][0], pk[qg][kc][1], pk[qg][kc][2], pk[qg][kc][3]};
+                    S.acc[qg][db] = M::mma(vf[kc][db], as_v8(pp), S.acc[qg][db]);
+                }
+    }
+
+    static __device__ void run(const FwdArgs &a) {
+        extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+        const int N = a.N;
+        const int logical = xcd_contiguous(blockIdx.x, a.total);
+        const int bh = logical / a.n_qtiles;
+        const int t_ = logical - bh * a.n_qtiles;
+        const int qt = CAUSAL ? a.n_qtiles - 1 - t_ : t_;  // causal: longest rows first
+        const size_t head = (size_t)bh * (size_t)N * D;
+        const uint16_t *Qh = static_cast<const uint16_t *>(a.q) + head;
+        const char *Kh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head);
+        const char *Vh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head);
+
+        const int tid = threadIdx.x;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+        const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+        const int q0 = qt * BR + w * QW;  // first query row of this wave
+
+        // A negative scale is applied as -|c| by negating Q (exact), so c >= 0 below.
+        float c = a.c;
+        uint32_t qsign = 0u;
+        if (c < 0.f) {
+            c = -c;
+            qsign = 0x80008000u;
+        }
+
+        State S;
+        // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its rows q
+        // (rows past the end read row N-1 and are zeroed).
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            const int q = q0 + 32 * qg + l32;
+            const uint32_t keep = q < N ? 0xffffffffu : 0u;
+            const uint16_t *qrow = Qh + (size_t)min(q, N - 1) * D + g * 8;
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + cc * 16);
+                x = (x & keep) ^ qsign;
+                S.qf[qg][cc] = as_v8(x);
+            }
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int quad = 0; quad < 4; ++quad) {
-                    v4 y;
+                for (int i = 0; i < 16; ++i) S.acc[qg][b][i] = 0.f;
+            S.m_ref[qg] = -INFINITY;
+            S.lsum[qg] = 0.f;
+        }
+        // Fragment read offsets.  K: lane reads chunk 2 cc + g of LDS row l32, stored at
+        // chunk (2 cc + g) ^ kswz(l32); kswz only reaches bits the k-step index does not
+        // share with the row term, so offset(cc) = offset(0) ^ (cc << 5).
+        // V^T: 16-lane group grp reads rows r_lane + 4 t + 16 kc at chunk 4 db + c_lane,
+        // stored at chunk (4 db + c_lane) ^ vswz(r_lane), which is offset(0) ^ (db << 6).
+        S.kfrag = l32 * ROWB + ((g ^ (kswz(l32) & 1)) << 4) + ((kswz(l32) >> 1) << 5);
+        {
+            const int j16 = lane & 15, grp = lane >> 4;
+            const int r_lane = 8 * (grp >> 1) + (j16 >> 2);
+            const int c_lane = 2 * (grp & 1) + ((j16 & 3) >> 1);
+            S.vfrag = TILE_B + r_lane * ROWB + ((c_lane ^ vswz(r_lane)) << 4) + 8 * (j16 & 1);
+        }
+        // Tile loads: lane fills LDS slot s with chunk (slot ^ swizzle) of K row
+        // sigma(row) and of V row row.  Offsets are tile relative: row * ROWB + chunk * 16.
+        uint32_t kld[LOADS], vld[LOADS];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) y[e] = static_cast<T>(acc[b][quad * 4 + e] * inv);
-                    *reinterpret_cast<v4 *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
+        for (int i = 0; i < LOADS; ++i) {
+            const int s = (w * LOADS + i) * 64 + lane;
+            const int r = s / CH, p = s % CH;
+            kld[i] = ((r & ~31) | swap_bits23(r & 31)) * ROWB + ((p ^ kswz(r)) << 4);
+            vld[i] = r * ROWB + ((p ^ vswz(r)) << 4);
+        }
+
+        const int n_kv_all = (N + BC - 1) / BC;
+        const int n_kv = CAUSAL ? min(n_kv_all, (qt * BR + BR - 1) / BC + 1) : n_kv_all;
+
+        auto issue_loads = [&](int j) {
+            const int k0 = j * BC;
+            unsigned char *st = smem + (j & 1) * STAGE_B;
+            const char *kt = Kh + (size_t)k0 * ROWB;
+            const char *vt = Vh + (size_t)k0 * ROWB;
+            if (k0 + BC <= N) {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_global_load_lds((const void *)(kt + kld[i]),
+                                                     (lds_void_t *)(st + (w * LOADS + i) * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const void *)(vt + vld[i]),
+                                                     (lds_void_t *)(st + TILE_B + (w * LOADS + i) * 1024), 16, 0, 0);
                 }
-            if (g == 0) a.lse[(size_t)bh * N + qrow] = (m + fast_log2(ltot)) * kLn2;
+            } else {  // last, partial tile: rows past the end read row N-1 (their scores are masked)
+                const uint32_t last = (uint32_t)(N - 1 - k0) * ROWB;
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    const uint32_t kr = kld[i] & ~(uint32_t)(ROWB - 1), vr = vld[i] & ~(uint32_t)(ROWB - 1);
+                    const uint32_t ko = min(kr, last) + (kld[i] & (ROWB - 1));
+                    const uint32_t vo = min(vr, last) + (vld[i] & (ROWB - 1));
+                    __builtin_amdgcn_global_load_lds((const void *)(kt + ko),
+                                                     (lds_void_t *)(st + (w * LOADS + i) * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const void *)(vt + vo),
+                                                     (lds_void_t *)(st + TILE_B + (w * LOADS + i) * 1024), 16, 0, 0);
+                }
+            }
+        };
+
+        // Tiles [0, j_plain) are fully visible to every row of this wave; the rest
+        // cross its diagonal, hold the end of the sequence, or (causal) lie wholly
+        // after its rows and are skipped.  Two loops keep one tile body per loop.
+        const int j_plain = min(n_kv, min(CAUSAL ? (q0 + 1) / BC : n_kv, N / BC));
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+        auto next = [&](int j) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // tile j is in LDS; every wave is done with tile j-1
+            if (j + 1 < n_kv) issue_loads(j + 1);
+        };
+        issue_loads(0);
+        int j = 0;
+        for (; j < j_plain; ++j) {
+            next(j);
+            tile<false>(S, lds0 + (j & 1) * STAGE_B, j * BC, q0, N, c, l32, g);
+        }
+        for (; j < n_kv; ++j) {
+            next(j);
+            const int k0 = j * BC;
+            if (CAUSAL && k0 > q0 + QW - 1) continue;  // every key after every row of this wave
+            tile<true>(S, lds0 + (j & 1) * STAGE_B, k0, q0, N, c, l32, g);
+        }
+
+        // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
+        // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q.
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            const int q = q0 + 32 * qg + l32;
+            const float ltot = lane_swap32_add(S.lsum[qg]);
+            if (q < N) {
+                const float inv = 1.f / ltot;
+                uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+#pragma unroll
+                    for (int quad = 0; quad < 4; ++quad) {
+                        const uint32_t lo = M::pack(S.acc[qg][b][quad * 4 + 0] * inv, S.acc[qg][b][quad * 4 + 1] * inv);
+                        const uint32_t hi = M::pack(S.acc[qg][b][quad * 4 + 2] * inv, S.acc[qg][b][quad * 4 + 3] * inv);
+                        const u32x2_t y = {lo, hi};
+                        *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
+                    }
+                if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref[qg] + fast_log2(ltot)) * kLn2;
+            }
         }
     }
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2)
+__global__ __launch_bounds__(512, 1)
 void attn_fwd_mfma_kernel(FwdArgs a) {
-    static_assert(MfmaFwd<T, D, CAUSAL>::THREADS == 256, "launch bounds assume 256 threads");
+    static_assert(MfmaFwd<T, D, CAUSAL>::THREADS == 512, "launch bounds assume 512 threads");
     MfmaFwd<T, D, CAUSAL>::run(a);
 }
 
