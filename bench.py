@@ -57,6 +57,53 @@ def measured_traffic(workload_name: str):
         return None
 
 
+def _counter_avg(path: str, counter: str, name_part: str) -> float:
+    """Mean per-dispatch value of a rocprofv3 --pmc counter for kernels whose name contains name_part."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{name_part}' in {path}")
+    return sum(vals) / len(vals)
+
+
+def summarize_traffic(args) -> None:
+    """Write the HBM traffic summary from two attention runs (FETCH_SIZE, WRITE_SIZE) and the
+    same two counters on a plain device copy of known size (calibration)."""
+    from exact_attention_96_amd.workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    kern = "attn_fwd_mfma_kernel" if w.dtype != "f32" else "attn_fwd_f32_kernel"
+    fetch_kib = _counter_avg(args.fetch_csv, "FETCH_SIZE", kern)
+    write_kib = _counter_avg(args.write_csv, "WRITE_SIZE", kern)
+    copy_fetch_kib = _counter_avg(args.copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    copy_write_kib = _counter_avg(args.copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    fetch_factor = args.copy_bytes / (copy_fetch_kib * 1024)
+    write_factor = args.copy_bytes / (copy_write_kib * 1024)
+    hbm = fetch_kib * 1024 * fetch_factor + write_kib * 1024 * write_factor
+    lines = [
+        f"# HBM traffic of {kern} on {w.name}",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (rocprofv3 --pmc, one counter per run),",
+        "# scaled by the ratio of known bytes to counter bytes on a device copy of copy_bytes.",
+        f"workload = {w.name}",
+        f"kernel_source_sha = {kernel_source_hash()}",
+        f"fetch_kib_per_dispatch = {fetch_kib:.1f}",
+        f"write_kib_per_dispatch = {write_kib:.1f}",
+        f"copy_bytes = {args.copy_bytes}",
+        f"copy_fetch_kib = {copy_fetch_kib:.1f}",
+        f"copy_write_kib = {copy_write_kib:.1f}",
+        f"fetch_factor = {fetch_factor:.4f}",
+        f"write_factor = {write_factor:.4f}",
+        f"hbm_bytes_per_launch = {hbm:.0f}",
+        f"algorithmic_bytes_per_launch = {w.io_bytes}",
+        f"traffic_over_algorithmic = {hbm / w.io_bytes:.3f}",
+    ]
+    if args.commands:
+        lines += ["# commands:"] + [f"#   {c}" for c in args.commands]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, q, k, v, budget_heads: int):
     """The fp64 oracle (as it stands) on whole heads of the same workload."""
     import oracle
@@ -94,7 +141,20 @@ def main():
                     help="heads of the workload the CPU oracle runs for cpu_baseline (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of this many bytes (counter calibration)")
+    ap.add_argument("--summarize-traffic", action="store_true",
+                    help="write the HBM traffic summary from rocprofv3 counter CSVs and exit")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--copy-fetch-csv")
+    ap.add_argument("--copy-write-csv")
+    ap.add_argument("--copy-bytes", type=int, default=268435456)
+    ap.add_argument("--out", default=TRAFFIC_FILE)
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward is not sharded across "
