@@ -37,7 +37,7 @@ hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
     FwdArgs b = a;
     b.n_qtiles = (a.N + K::BR - 1) / K::BR;
     b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
-    constexpr int lds_bytes = 2 * K::STAGE_B;
+    constexpr int lds_bytes = K::LDS_B;
     // opt in to the LDS size once per kernel (thread-safe static initialisation)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>),

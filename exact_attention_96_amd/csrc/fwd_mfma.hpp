@@ -4,18 +4,18 @@
 // loop over row blocks of Q, inner loop over column blocks of K and V).  One
 // workgroup owns one (batch*head, query tile) pair of BR = 256 query rows;
 // each of its 4 waves (one per SIMD) owns 64 rows as two groups of 32.  The
-// inner loop walks keys in tiles of BC = 64, and per tile every wave applies
-// the update of that page's section "两块情况的完整推导" (steps 5-7): row max,
-// rescale of the running sum and of the unnormalised output, P V; after the
-// last tile it divides by the row sum (step 8) and writes the row
+// inner loop walks keys in tiles of BC = 64; per tile and row group it
+// applies the update of that page's section "两块情况的完整推导" (steps 5-7):
+// row max, rescale of the running sum and of the unnormalised output, P V;
+// after the last tile it divides by the row sum (step 8) and writes the row
 // log-sum-exp (appendix "附：数值稳定的logsumexp(L)推导").
 //
 // Data movement.  K and V tiles go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging), double buffered: the loads
-// of tile j+1 are in flight while tile j is computed, with one barrier per
-// tile.  Both tiles keep their row-major layout, each 16-byte chunk of a row
-// placed at chunk index XOR a row-dependent swizzle so that every fragment
-// read below is free of LDS bank conflicts.
+// global_load_lds_dwordx4 (no register staging): two K stages and three V
+// stages, one barrier per tile, the loads of tile j+1 in flight while tile j
+// is computed.  Rows keep their row-major layout with each 16-byte chunk
+// placed at chunk index XOR a row-dependent swizzle, which makes every
+// fragment read below free of LDS bank conflicts.
 //
 // First product, transposed: S^T = K Q^T with v_mfma_f32_32x32x16.  Q^T is the
 // B operand, held in registers for the whole loop.  Its accumulator gives
@@ -28,6 +28,16 @@
 // to the matrix core without leaving registers, and the per-row rescale of O^T
 // is a per-lane multiply.  The V^T A operand comes from the row-major V tile
 // through ds_read_b64_tr_b16 (each 16-lane group transposes a 4 x 16 block).
+//
+// Software pipeline.  With two independent row groups per wave, every phase
+// of a tile pairs one MFMA stream with VALU work of the other group:
+//     A: S_0(j)     | pack + row sum of group 1, tile j-1;  then row max of group 0
+//     B: PV_1(j-1)  | exponentials of group 0, tile j
+//     C: S_1(j)     | pack + row sum of group 0, tile j;    then row max of group 1
+//     D: PV_0(j)    | exponentials of group 1, tile j
+// so the matrix cores stay busy while the softmax runs on the vector ALUs.
+// Tiles that cross the diagonal or the end of the sequence (the last few of
+// a wave) run unpipelined, after the pipeline is drained.
 //
 // Softmax arithmetic.  t = s * c with c = scale * log2(e); p = 2^(t - m).
 // The reference m is only moved when a tile's row max exceeds it by more than
@@ -62,7 +72,6 @@ template <typename T> struct Mfma;
 
 template <> struct Mfma<__bf16> {
     typedef bf16x8_t v8;
-    typedef bf16x4_t v4;
     typedef bf16x2_t v2;
     static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -76,7 +85,6 @@ template <> struct Mfma<__bf16> {
 
 template <> struct Mfma<_Float16> {
     typedef f16x8_t v8;
-    typedef f16x4_t v4;
     typedef f16x2_t v2;
     static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -107,21 +115,30 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-template <typename T, int D, bool CAUSAL, int QG = 1>
+// sched_group_barrier masks
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// Materialise a value in a VGPR at this point of the program.  The empty asm
+// has no cost; it keeps the compiler from sinking the value's computation into
+// a later block (the software pipeline below places work deliberately).
+__device__ __forceinline__ void pin(float &x) { asm("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t &x) { asm("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x16_t &x) { asm("" : "+v"(x)); }
+
+template <typename T, int D, bool CAUSAL>
 struct MfmaFwd {
-    static constexpr int NW = 8 / QG;          // waves per workgroup
-    static constexpr int QW = 32 * QG;         // query rows per wave (QG groups of 32)
-    static constexpr int BR = NW * QW;         // query rows per workgroup (256)
-    static constexpr int BC = 64;              // keys per tile
+    static constexpr int NW = 8;               // waves per workgroup, two per SIMD
+    static constexpr int BR = NW * 32;         // query rows per workgroup (256), 32 per wave
+    static constexpr int BC = 64;              // keys per tile, as two 32-key halves
     static constexpr int THREADS = NW * 64;
     static constexpr int CH = D / 8;           // 16-byte chunks per row
     static constexpr int ROWB = D * 2;         // bytes per K/V row
     static constexpr int TILE_B = BC * ROWB;   // bytes per K or V tile
-    static constexpr int STAGE_B = 2 * TILE_B; // K tile then V tile
-    static constexpr int LOADS = BC * CH / 64 / NW;  // 16-byte-per-lane loads per wave per tile
+    static constexpr int STAGES = 2;           // LDS stages (K tile + V tile each)
+    static constexpr int LDS_B = STAGES * 2 * TILE_B;
+    static constexpr int LOADS = BC * CH / 64 / NW;  // 16-byte-per-lane loads per wave per tile and tensor
     static constexpr int DB = D / 32;          // 32-row blocks of O^T
     static constexpr int DC = D / 16;          // k-steps of the first product
-    static constexpr int KC = BC / 16;         // k-steps of the second product
     static constexpr float TAU = 8.0f;
     typedef Mfma<T> M;
     typedef typename M::v8 v8;
@@ -132,90 +149,40 @@ struct MfmaFwd {
 
     static __device__ __forceinline__ v8 as_v8(u32x4_t x) { return __builtin_bit_cast(v8, x); }
 
+    typedef uint32_t Packed[2][4];  // one 32-key half as two 16-key B operands
+
     // State a wave carries across key tiles.
     struct State {
-        v8 qf[QG][DC];           // Q^T fragments of the wave's row groups
-        f32x16_t acc[QG][DB];    // unnormalised O^T
-        float m_ref[QG];         // reference row max (log2 domain)
-        float lsum[QG];          // this lane's share of the row sums
+        v8 qf[DC];               // Q^T fragments of the wave's 32 rows
+        f32x16_t acc[DB];        // unnormalised O^T
+        float m_ref;             // reference row max (log2 domain)
+        float lsum;              // this lane's share of the row sum
         uint32_t kfrag;          // LDS byte offset of K fragment k-step 0 (k-step cc: ^ cc << 5)
         uint32_t vfrag;          // LDS byte offset of V^T fragment block 0 (block db: ^ db << 6)
+        float c;                 // scale * log2(e), >= 0
+        int q0, N, l32, g;       // first row of the wave, sequence length, lane coordinates
     };
 
-    // One key tile for one wave.  MASKED: the tile crosses the diagonal or the
-    // end of the sequence, so scores of invisible keys are dropped.
-    template <bool MASKED>
-    static __device__ __forceinline__ void tile(State &S, uint32_t st, int k0, int q0, int N,
-                                                float c, int l32, int g) {
-        const uint32_t kbase = S.kfrag + st, vbase = S.vfrag + st;
-        // ---- S^T = K Q^T: two 32-key blocks x QG 32-row groups
-        f32x16_t s[QG][2];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[qg][kb][i] = 0.f;
-        // all K fragments of the tile are requested before the first MFMA
-        v8 kf[2][DC];
-#pragma unroll
-        for (int cc = 0; cc < DC; ++cc)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                kf[kb][cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)((kbase ^ (cc << 5)) + kb * 32 * ROWB));
-#pragma unroll
-        for (int cc = 0; cc < DC; ++cc)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) s[qg][kb] = M::mma(kf[kb][cc], S.qf[qg][cc], s[qg][kb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DC, 0);      // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DC * QG, 0); // then the MFMAs
+    // ------------------------------------------------------------ building blocks
 
-        // ---- visibility of register i of block kb: key k0 + 32 kb + (i & 7) + 8 g + 16 (i >> 3)
-        auto visible = [&](int qg, int kb, int i) {
-            const int key = k0 + 32 * kb + (i & 7) + 8 * g + 16 * (i >> 3);
-            const int q = q0 + 32 * qg + l32;
-            return key < N && (!CAUSAL || key <= q);
-        };
+    // S^T for the 32 keys of half h of the tile at LDS address st
+    static __device__ __forceinline__ f32x16_t s_half(const State &S, uint32_t st, int h) {
+        const uint32_t kbase = S.kfrag + st + h * 32 * ROWB;
+        v8 kf[DC];
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) kf[cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)(kbase ^ (cc << 5)));
+        f32x16_t s = {};
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) s = M::mma(kf[cc], S.qf[cc], s);
+        return s;
+    }
 
-        // ---- row max per group
-        float mt[QG];
+    // O^T += V^T P^T for the 32 keys of half h (V tile at LDS address st + TILE_B)
+    static __device__ __forceinline__ void pv_half(State &S, uint32_t st, int h, const Packed &pk) {
+        const uint32_t vbase = S.vfrag + st + TILE_B + h * 32 * ROWB;
+        v8 vf[2][DB];
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float x = s[qg][kb][i];
-                    mx = fmaxf(mx, MASKED ? (visible(qg, kb, i) ? x : -INFINITY) : x);
-                }
-            mx = lane_swap32_max(mx);
-            mt[qg] = MASKED ? (mx == -INFINITY ? -INFINITY : mx * c) : mx * c;
-        }
-        // ---- move the reference max only when a row max outgrows it by TAU
-        bool grow = false;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) grow = grow || (mt[qg] > S.m_ref[qg] + TAU);
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                const float m_new = fmaxf(S.m_ref[qg], mt[qg]);
-                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref[qg] - m_new);
-                S.lsum[qg] *= alpha;
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) S.acc[qg][b][i] *= alpha;
-                S.m_ref[qg] = m_new;
-            }
-        }
-
-        // ---- V^T fragments requested now; their latency hides behind the exponentials
-        v8 vf[KC][DB];
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const uint32_t vb = (vbase ^ (db << 6)) + kc * 16 * ROWB;
@@ -224,43 +191,98 @@ struct MfmaFwd {
                 const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
                 vf[kc][db] = as_v8((u32x4_t){l2[0], l2[1], h2[0], h2[1]});
             }
-
-        // ---- P = 2^(s c - m), rounded to T in pairs; row sums from the rounded pairs
-        uint32_t pk[QG][KC][4];
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            const float nm = S.m_ref[qg] == -INFINITY ? 0.f : -S.m_ref[qg];
-            float rs = 0.f;
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i0 = 8 * h + 2 * e;
-                        float p0 = fast_exp2(fmaf(s[qg][kb][i0], c, nm));
-                        float p1 = fast_exp2(fmaf(s[qg][kb][i0 + 1], c, nm));
-                        if (MASKED) {
-                            p0 = visible(qg, kb, i0) ? p0 : 0.f;
-                            p1 = visible(qg, kb, i0 + 1) ? p1 : 0.f;
-                        }
-                        pk[qg][2 * kb + h][e] = M::pack(p0, p1);
-                        rs += p0 + p1;
-                    }
-            S.lsum[qg] += rs;
-        }
-
-        // ---- O^T += V^T P^T, 16 keys per MFMA; each V fragment serves every row group
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) {
-                    const u32x4_t pp = {pk[qg][kc][0], pk[qg][kc][1], pk[qg][kc][2], pk[qg][kc][3]};
-                    S.acc[qg][db] = M::mma(vf[kc][db], as_v8(pp), S.acc[qg][db]);
-                }
+            for (int db = 0; db < DB; ++db) {
+                const u32x4_t pp = {pk[kc][0], pk[kc][1], pk[kc][2], pk[kc][3]};
+                S.acc[db] = M::mma(vf[kc][db], as_v8(pp), S.acc[db]);
+            }
     }
+
+    // is the key of accumulator register i of half h visible to this lane's row?
+    static __device__ __forceinline__ bool visible(const State &S, int k0, int h, int i) {
+        const int key = k0 + 32 * h + (i & 7) + 8 * S.g + 16 * (i >> 3);
+        return key < S.N && (!CAUSAL || key <= S.q0 + S.l32);
+    }
+
+    // row max of a half in the log2 domain (-inf when nothing is visible)
+    template <bool MASKED>
+    static __device__ __forceinline__ float row_max(const State &S, const f32x16_t &s, int k0, int h) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, MASKED ? (visible(S, k0, h, i) ? s[i] : -INFINITY) : s[i]);
+        mx = lane_swap32_max(mx);
+        return MASKED ? (mx == -INFINITY ? -INFINITY : mx * S.c) : mx * S.c;
+    }
+
+    // p = 2^(s c - m) in place
+    template <bool MASKED>
+    static __device__ __forceinline__ void exponentials(const State &S, f32x16_t &s, int k0, int h) {
+        const float nm = S.m_ref == -INFINITY ? 0.f : -S.m_ref;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float p = fast_exp2(fmaf(s[i], S.c, nm));
+            if (MASKED) p = visible(S, k0, h, i) ? p : 0.f;
+            s[i] = p;
+        }
+    }
+
+    // round p to T in pairs (two 16-key B operands) and add the fp32 p to the row sum
+    static __device__ __forceinline__ void pack_sum(State &S, const f32x16_t &p, Packed &pk) {
+        float rs = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = p[8 * kc + 2 * e], p1 = p[8 * kc + 2 * e + 1];
+                pk[kc][e] = M::pack(p0, p1);
+                rs += p0 + p1;
+            }
+        S.lsum += rs;
+    }
+
+    // Move the reference max to mt if it outgrew it by TAU; returns the factor applied.
+    static __device__ __forceinline__ bool grow(const State &S, float mt) {
+        return __builtin_amdgcn_ballot_w64(mt > S.m_ref + TAU) != 0;
+    }
+    static __device__ __forceinline__ float rescale(State &S, float mt) {
+        const float m_new = fmaxf(S.m_ref, mt);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
+        S.lsum *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
+        S.m_ref = m_new;
+        return alpha;
+    }
+
+    // One key tile for one wave, as two 32-key halves:
+    //   S(h0); max; [rescale];  exp(h0) | S(h1);  max; [rescale incl. pending p(h0)];
+    //   pack(h0) + exp(h1) | PV(h0);  pack(h1) | PV(h1)
+    template <bool MASKED>
+    static __device__ __forceinline__ void tile(State &S, uint32_t st, int k0) {
+        f32x16_t s0 = s_half(S, st, 0);
+        const float mt0 = row_max<MASKED>(S, s0, k0, 0);
+        if (grow(S, mt0)) rescale(S, mt0);
+        exponentials<MASKED>(S, s0, k0, 0);
+        f32x16_t s1 = s_half(S, st, 1);
+        const float mt1 = row_max<MASKED>(S, s1, k0, 1);
+        if (grow(S, mt1)) {
+            const float alpha = rescale(S, mt1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s0[i] *= alpha;  // p(h0) joins the new reference
+        }
+        Packed pk0, pk1;
+        pack_sum(S, s0, pk0);
+        exponentials<MASKED>(S, s1, k0, 1);
+        pv_half(S, st, 0, pk0);
+        pack_sum(S, s1, pk1);
+        pv_half(S, st, 1, pk1);
+    }
+
+    // ------------------------------------------------------------ kernel body
 
     static __device__ void run(const FwdArgs &a) {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -278,40 +300,39 @@ struct MfmaFwd {
         const int tid = threadIdx.x;
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
         const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-        const int q0 = qt * BR + w * QW;  // first query row of this wave
 
+        State S;
+        S.q0 = qt * BR + w * 32;
+        S.N = N;
+        S.l32 = l32;
+        S.g = g;
         // A negative scale is applied as -|c| by negating Q (exact), so c >= 0 below.
-        float c = a.c;
+        S.c = a.c;
         uint32_t qsign = 0u;
-        if (c < 0.f) {
-            c = -c;
+        if (S.c < 0.f) {
+            S.c = -S.c;
             qsign = 0x80008000u;
         }
 
-        State S;
-        // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its rows q
+        // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its row q
         // (rows past the end read row N-1 and are zeroed).
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            const int q = q0 + 32 * qg + l32;
+        {
+            const int q = S.q0 + l32;
             const uint32_t keep = q < N ? 0xffffffffu : 0u;
             const uint16_t *qrow = Qh + (size_t)min(q, N - 1) * D + g * 8;
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
                 u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + cc * 16);
                 x = (x & keep) ^ qsign;
-                S.qf[qg][cc] = as_v8(x);
+                S.qf[cc] = as_v8(x);
             }
         }
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) S.acc[qg][b][i] = 0.f;
-            S.m_ref[qg] = -INFINITY;
-            S.lsum[qg] = 0.f;
-        }
+            for (int i = 0; i < 16; ++i) S.acc[b][i] = 0.f;
+        S.m_ref = -INFINITY;
+        S.lsum = 0.f;
         // Fragment read offsets.  K: lane reads chunk 2 cc + g of LDS row l32, stored at
         // chunk (2 cc + g) ^ kswz(l32); kswz only reaches bits the k-step index does not
         // share with the row term, so offset(cc) = offset(0) ^ (cc << 5).
@@ -322,7 +343,7 @@ struct MfmaFwd {
             const int j16 = lane & 15, grp = lane >> 4;
             const int r_lane = 8 * (grp >> 1) + (j16 >> 2);
             const int c_lane = 2 * (grp & 1) + ((j16 & 3) >> 1);
-            S.vfrag = TILE_B + r_lane * ROWB + ((c_lane ^ vswz(r_lane)) << 4) + 8 * (j16 & 1);
+            S.vfrag = r_lane * ROWB + ((c_lane ^ vswz(r_lane)) << 4) + 8 * (j16 & 1);
         }
         // Tile loads: lane fills LDS slot s with chunk (slot ^ swizzle) of K row
         // sigma(row) and of V row row.  Offsets are tile relative: row * ROWB + chunk * 16.
@@ -337,19 +358,21 @@ struct MfmaFwd {
 
         const int n_kv_all = (N + BC - 1) / BC;
         const int n_kv = CAUSAL ? min(n_kv_all, (qt * BR + BR - 1) / BC + 1) : n_kv_all;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
 
         auto issue_loads = [&](int j) {
             const int k0 = j * BC;
-            unsigned char *st = smem + (j & 1) * STAGE_B;
+            unsigned char *ks = smem + (j % STAGES) * 2 * TILE_B;
+            unsigned char *vs = ks + TILE_B;
             const char *kt = Kh + (size_t)k0 * ROWB;
             const char *vt = Vh + (size_t)k0 * ROWB;
             if (k0 + BC <= N) {
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     __builtin_amdgcn_global_load_lds((const void *)(kt + kld[i]),
-                                                     (lds_void_t *)(st + (w * LOADS + i) * 1024), 16, 0, 0);
+                                                     (lds_void_t *)(ks + (w * LOADS + i) * 1024), 16, 0, 0);
                     __builtin_amdgcn_global_load_lds((const void *)(vt + vld[i]),
-                                                     (lds_void_t *)(st + TILE_B + (w * LOADS + i) * 1024), 16, 0, 0);
+                                                     (lds_void_t *)(vs + (w * LOADS + i) * 1024), 16, 0, 0);
                 }
             } else {  // last, partial tile: rows past the end read row N-1 (their scores are masked)
                 const uint32_t last = (uint32_t)(N - 1 - k0) * ROWB;
@@ -359,56 +382,52 @@ struct MfmaFwd {
                     const uint32_t ko = min(kr, last) + (kld[i] & (ROWB - 1));
                     const uint32_t vo = min(vr, last) + (vld[i] & (ROWB - 1));
                     __builtin_amdgcn_global_load_lds((const void *)(kt + ko),
-                                                     (lds_void_t *)(st + (w * LOADS + i) * 1024), 16, 0, 0);
+                                                     (lds_void_t *)(ks + (w * LOADS + i) * 1024), 16, 0, 0);
                     __builtin_amdgcn_global_load_lds((const void *)(vt + vo),
-                                                     (lds_void_t *)(st + TILE_B + (w * LOADS + i) * 1024), 16, 0, 0);
+                                                     (lds_void_t *)(vs + (w * LOADS + i) * 1024), 16, 0, 0);
                 }
             }
         };
-
-        // Tiles [0, j_plain) are fully visible to every row of this wave; the rest
-        // cross its diagonal, hold the end of the sequence, or (causal) lie wholly
-        // after its rows and are skipped.  Two loops keep one tile body per loop.
-        const int j_plain = min(n_kv, min(CAUSAL ? (q0 + 1) / BC : n_kv, N / BC));
-        const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
         auto next = [&](int j) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();  // tile j is in LDS; every wave is done with tile j-1
             if (j + 1 < n_kv) issue_loads(j + 1);
         };
+
+        // Tiles [0, j_plain) are fully visible to every row of this wave; the rest
+        // cross its diagonal, hold the end of the sequence, or (causal) lie wholly
+        // after its rows and are skipped.  Two loops keep one tile body per loop.
+        const int j_plain = min(n_kv, min(CAUSAL ? (S.q0 + 1) / BC : n_kv, N / BC));
         issue_loads(0);
         int j = 0;
         for (; j < j_plain; ++j) {
             next(j);
-            tile<false>(S, lds0 + (j & 1) * STAGE_B, j * BC, q0, N, c, l32, g);
+            tile<false>(S, lds0 + (j % STAGES) * 2 * TILE_B, j * BC);
         }
         for (; j < n_kv; ++j) {
             next(j);
             const int k0 = j * BC;
-            if (CAUSAL && k0 > q0 + QW - 1) continue;  // every key after every row of this wave
-            tile<true>(S, lds0 + (j & 1) * STAGE_B, k0, q0, N, c, l32, g);
+            if (CAUSAL && k0 > S.q0 + 31) continue;  // every key after every row of this wave
+            tile<true>(S, lds0 + (j % STAGES) * 2 * TILE_B, k0);
         }
 
         // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
         // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q.
+        const int q = S.q0 + l32;
+        const float ltot = lane_swap32_add(S.lsum);
+        if (q < N) {
+            const float inv = 1.f / ltot;
+            uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            const int q = q0 + 32 * qg + l32;
-            const float ltot = lane_swap32_add(S.lsum[qg]);
-            if (q < N) {
-                const float inv = 1.f / ltot;
-                uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
+            for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int quad = 0; quad < 4; ++quad) {
-                        const uint32_t lo = M::pack(S.acc[qg][b][quad * 4 + 0] * inv, S.acc[qg][b][quad * 4 + 1] * inv);
-                        const uint32_t hi = M::pack(S.acc[qg][b][quad * 4 + 2] * inv, S.acc[qg][b][quad * 4 + 3] * inv);
-                        const u32x2_t y = {lo, hi};
-                        *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
-                    }
-                if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref[qg] + fast_log2(ltot)) * kLn2;
-            }
+                for (int quad = 0; quad < 4; ++quad) {
+                    const uint32_t lo = M::pack(S.acc[b][quad * 4 + 0] * inv, S.acc[b][quad * 4 + 1] * inv);
+                    const uint32_t hi = M::pack(S.acc[b][quad * 4 + 2] * inv, S.acc[b][quad * 4 + 3] * inv);
+                    const u32x2_t y = {lo, hi};
+                    *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
+                }
+            if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
         }
     }
 };
