@@ -104,18 +104,23 @@ def summarize_traffic(args) -> None:
     print("\n".join(lines))
 
 
-def cpu_baseline(w, q, k, v, budget_heads: int):
-    """The fp64 oracle (as it stands) on whole heads of the same workload."""
+def cpu_baseline(w, q, k, v, seconds: float):
+    """The fp64 oracle (as it stands) on whole heads of the same workload, head after
+    head until `seconds` of wall time have been spent (at least one head)."""
     import oracle
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:budget_heads]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
     t0 = time.perf_counter()
     for (b, h) in heads:
         oracle.attn_rows(q[b, h], k[b, h], v[b, h], w.scale, w.causal, range(w.N))
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
-    flops = w.flops * len(heads) / (w.B * w.H)
+    flops = w.flops * done / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(heads)} of {w.B * w.H} heads, all {w.N} query rows each "
+            "sample": f"{done} of {w.B * w.H} heads, all {w.N} query rows each "
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
 
@@ -137,8 +142,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", help="c1..c5 (default: c3, the headline)")
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="heads of the workload the CPU oracle runs for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time the CPU oracle runs whole heads for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=None, help="(0: skip the cpu_baseline leg)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of this many bytes (counter calibration)")
     ap.add_argument("--summarize-traffic", action="store_true",
@@ -227,9 +233,9 @@ def main():
                      "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
                      "kernel_source_sha": kernel_source_hash()},
     }
-    if args.cpu_heads > 0:
-        print(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads)
+    if args.cpu_seconds > 0 and args.cpu_heads != 0:
+        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
