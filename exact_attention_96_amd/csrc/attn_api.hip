@@ -33,7 +33,7 @@ hipError_t launch_f32(const FwdArgs &a, int bh, hipStream_t stream) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
-    typedef attn::MfmaFwd<T, D, CAUSAL, attn::kRowGroups> K;
+    typedef attn::MfmaFwd<T, D, CAUSAL> K;
     FwdArgs b = a;
     b.n_qtiles = (a.N + K::BR - 1) / K::BR;
     b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd

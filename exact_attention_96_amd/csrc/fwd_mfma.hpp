@@ -3,20 +3,30 @@
 // Decomposition ("Understand FlashAttention", section "FlashAttention": outer
 // loop over row blocks of Q, inner loop over column blocks of K and V).  One
 // workgroup owns one (batch*head, query tile) pair of BR = 256 query rows;
-// each of its 8 waves (two per SIMD) owns 32 rows.  The inner loop walks keys
-// in tiles of BC = 128, and for every 32 keys of a tile it applies the update
-// of that page's section "两块情况的完整推导" (steps 5-7): row max, rescale of
-// the running sum and of the unnormalised output, P V; after the last tile it
-// divides by the row sum (step 8) and writes the row log-sum-exp (appendix
-// "附：数值稳定的logsumexp(L)推导").
+// each of its 8 waves owns 32 rows.  The inner loop walks keys in units of
+// BU = 64 and for each unit applies the update of that page's section
+// "两块情况的完整推导" (steps 5-7): row max, rescale of the running sum and of
+// the unnormalised output, P V; after the last unit it divides by the row sum
+// (step 8) and writes the row log-sum-exp (appendix "附：数值稳定的logsumexp(L)推导").
 //
-// Data movement.  K and V tiles go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging), two stages of K and of V,
-// one barrier per tile, the loads of tile j+1 in flight while tile j is
-// computed.  Rows keep their row-major layout with each 16-byte chunk placed
-// at chunk index XOR a row-dependent swizzle, which makes every fragment read
-// below free of LDS bank conflicts.  Fragment addresses are computed once;
-// stage, key block and k-step are immediate offsets of the LDS reads.
+// Ping-pong.  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 form two
+// groups that alternate between a matrix phase (the MFMAs of one unit: S of
+// unit u and P V of unit u - 1) and a softmax phase (exponentials of unit u on
+// the vector ALU); the second group runs one phase behind, and a workgroup
+// barrier separates phases.  So on every SIMD one wave feeds the matrix core
+// while the other computes exponentials.  During its softmax phase a wave also
+// reads the K fragments of its next unit from LDS into registers, so that the
+// score MFMAs of a matrix phase start without waiting for LDS; only the V^T
+// reads remain in the matrix phase, issued ahead of the P V MFMAs.
+//
+// Data movement.  K and V units go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging) into two rings of four stages;
+// the load group of unit u + 3 is issued at the start of step u and its
+// completion is awaited (explicit vmcnt counts) only at the barriers that
+// precede its first reader.  Rows keep their row-major layout with each
+// 16-byte chunk placed at chunk index XOR a row-dependent swizzle, which makes
+// every fragment read below free of LDS bank conflicts.  Fragment addresses are
+// computed once; stage, key half and key chunk are immediate offsets.
 //
 // First product, transposed: S^T = K Q^T with v_mfma_f32_32x32x16.  Q^T is the
 // B operand, held in registers for the whole loop.  Its accumulator gives
@@ -27,25 +37,20 @@
 // hold the consecutive keys 16h + 8g .. 16h + 8g + 7, which is exactly the B
 // operand layout of the second product O^T = V^T P^T: P goes from the softmax
 // to the matrix core without leaving registers, and the per-row rescale of O^T
-// is a per-lane multiply.  The V^T A operand comes from the row-major V tile
+// is a per-lane multiply.  The V^T A operand comes from the row-major V unit
 // through ds_read_b64_tr_b16 (each 16-lane group transposes a 4 x 16 block).
-//
-// Overlap.  Each 64 keys are processed as two 32-key halves so that the
-// scores of the second half (MFMA) are computed while the exponentials of the
-// first (VALU) run, and each half's P V (MFMA) overlaps the next VALU work; the
-// second wave on the SIMD fills the remaining gaps.  Tiles that cross the
-// diagonal or the end of the sequence (the last ones of a wave) run a masked
-// copy of the same body in a second loop, so the common loop has no masking.
 //
 // Softmax arithmetic.  t = s * c with c = scale * log2(e); p = 2^(t - m).
 // The reference m is only moved when a row max exceeds it by more than
 // TAU = 8 (in log2 units), so the O rescale runs a handful of times per row
-// instead of once per key block.  This changes no result: softmax is invariant
-// to the shift (same page, "数值稳定的 Softmax"), and p <= 2^8 keeps every
+// instead of once per unit.  This changes no result: softmax is invariant to
+// the shift (same page, "数值稳定的 Softmax"), and p <= 2^8 keeps every
 // intermediate far inside fp32/bf16/fp16 range.  The row sum adds the fp32
 // probabilities before their rounding to the input type, so lse keeps fp32
 // accuracy (a sum of bf16-rounded terms would cost ~2^-9 relative in l).
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -109,26 +114,59 @@ __device__ __forceinline__ float lane_swap32_add(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// V^T reads issued before the first score MFMA of a matrix phase
+constexpr int kGemmFirstReads = 8;
+
+// Scheduling groups: N single MFMAs, each followed by up to PER of the LEFT
+// remaining LDS reads.
+template <int N, int PER, int LEFT>
+__device__ __forceinline__ void sched_mfma_reads() {
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if constexpr (LEFT > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEFT < PER ? LEFT : PER, 0);
+        sched_mfma_reads<N - 1, PER, (LEFT > PER ? LEFT - PER : 0)>();
+    }
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory (base + voff) straight into LDS at
+// lds + 16 * lane (global_load_lds_dwordx4; base and lds wave-uniform).  Issued
+// from inline assembly so that the compiler does not order later LDS reads
+// after it: completion is tracked with explicit vmcnt waits.  M0 carries the LDS
+// address and is written here; nothing else in these kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see above
+__device__ __forceinline__ void dma_to_lds16(const void *base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-template <typename T, int D, bool CAUSAL, int QG>
+template <typename T, int D, bool CAUSAL>
 struct MfmaFwd {
-    static constexpr int NW = 8 / QG;          // waves per workgroup (2 per SIMD for QG = 1, 1 for QG = 2)
-    static constexpr int BR = NW * QG * 32;    // query rows per workgroup (256), 32 QG per wave
-    static constexpr int BC = 128;             // keys per tile, as four 32-key quarters
+    static constexpr int NW = 8;                     // waves per workgroup, two per SIMD
+    static constexpr int BR = NW * 32;               // query rows per workgroup, 32 per wave
+    static constexpr int BU = 64;                    // keys per unit (one matrix phase)
+    static constexpr int STAGES = 4;                 // LDS ring depth, for K and for V
     static constexpr int THREADS = NW * 64;
-    static constexpr int CH = D / 8;           // 16-byte chunks per row
-    static constexpr int ROWB = D * 2;         // bytes per K/V row
-    static constexpr int TILE_B = BC * ROWB;   // bytes per K or V tile
-    static constexpr int STAGES = 2;           // LDS stages (K tile + V tile each)
-    static constexpr int LDS_B = STAGES * 2 * TILE_B;
-    static constexpr int V_BASE = STAGES * TILE_B;  // V stages follow the K stages
-    static constexpr int LOADS = BC * CH / 64 / NW;  // 16-byte-per-lane loads per wave per tile and tensor
-    static constexpr int DB = D / 32;          // 32-row blocks of O^T
-    static constexpr int DC = D / 16;          // k-steps of the first product
+    static constexpr int CH = D / 8;                 // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;               // bytes per K/V row
+    static constexpr int UNIT_B = BU * ROWB;         // bytes per K or V unit
+    static constexpr int V_BASE = STAGES * UNIT_B;   // V ring follows the K ring
+    static constexpr int LDS_B = 2 * STAGES * UNIT_B;
+    static constexpr int LOADS = BU * CH / 64 / NW;  // 16-byte-per-lane DMA loads per wave, unit and tensor
+    static constexpr int GROUP = 2 * LOADS;          // DMA loads per wave in one load group
+    static constexpr int DB = D / 32;                // 32-row blocks of O^T
+    static constexpr int DC = D / 16;                // k-steps of the first product
     static constexpr float TAU = 8.0f;
+    static_assert(LOADS >= 1 && LOADS * 64 * NW == BU * CH, "unit loads split evenly over the waves");
+    static_assert(LDS_B <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 3, "waits assume at least three ring stages");
     typedef Mfma<T> M;
     typedef typename M::v8 v8;
 
@@ -138,173 +176,139 @@ struct MfmaFwd {
 
     static __device__ __forceinline__ v8 as_v8(u32x4_t x) { return __builtin_bit_cast(v8, x); }
 
-    typedef uint32_t Packed[2][4];  // one 32-key half as two 16-key B operands
+    typedef uint32_t Packed[2][2][4];  // P of one unit: [32-key half][16-key B operand][pair]
 
-    // State a wave carries across key tiles.
+    // State a wave carries across units.
     struct State {
-        v8 qf[QG][DC];           // Q^T fragments of the wave's row groups
-        f32x16_t acc[QG][DB];    // unnormalised O^T
-        float m_ref[QG];         // reference row max (log2 domain)
-        float lsum[QG];          // this lane's share of the row sums
+        v8 qf[DC];               // Q^T fragments of the wave's 32 rows
+        f32x16_t acc[DB];        // unnormalised O^T
+        float m_ref;             // reference row max (log2 domain)
+        float lsum;              // this lane's share of the row sum
         uint32_t kaddr[DC];      // LDS address of this lane's K fragment for k-step cc (stage 0)
         uint32_t vaddr[DB];      // LDS address of this lane's V^T fragment for d block db (stage 0)
         float c;                 // scale * log2(e), >= 0
-        int q0, N, l32, g;       // first row of the wave, sequence length, lane coordinates
+        int r0, N, l32, g;       // first row of the wave, sequence length, lane coordinates
     };
 
     // ------------------------------------------------------------ building blocks
 
-    // S^T for the 32 keys of half h of the tile in LDS stage ST, every row group
-    // (each K fragment feeds one MFMA per group).  Stage and half are immediate offsets.
-    template <int ST>
-    static __device__ __forceinline__ void s_half(const State &S, int h, f32x16_t (&s)[QG]) {
-        v8 kf[DC];
+    typedef v8 KFrags[2][DC];  // K fragments of one unit: [32-key half][k-step]
+
+    // K fragments of the unit in ring stage offset koff (read during the softmax
+    // phase before the matrix phase that uses them).
+    static __device__ __forceinline__ void kload(const State &S, KFrags &kf, uint32_t koff) {
 #pragma unroll
-        for (int cc = 0; cc < DC; ++cc)
-            kf[cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)(S.kaddr[cc] + ST * TILE_B + h * 32 * ROWB));
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) s[qg] = (f32x16_t){};
-#pragma unroll
-        for (int cc = 0; cc < DC; ++cc)
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) s[qg] = M::mma(kf[cc], S.qf[qg][cc], s[qg]);
+            for (int cc = 0; cc < DC; ++cc)
+                kf[h][cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)(S.kaddr[cc] + koff + h * 32 * ROWB));
     }
 
-    // O^T += V^T P^T for the 32 keys of half h of the tile in LDS stage ST, every
-    // row group (each V fragment feeds one MFMA per group)
-    template <int ST>
-    static __device__ __forceinline__ void pv_half(State &S, int h, const Packed (&pk)[QG]) {
-        v8 vf[2][DB];
+    // Matrix phase: S^T of unit u (K fragments already in registers) and
+    // O^T += V^T P^T of unit u - 1 (V in ring stage offset voff, P from the previous
+    // softmax phase).  The V^T reads are issued first; the score MFMAs, which need no
+    // LDS data, run while they are in flight.
+    static __device__ __forceinline__ void gemm(State &S, f32x16_t (&s)[2], const Packed &pk, const KFrags &kf,
+                                                uint32_t voff) {
+        v8 vf[2][2][DB];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const uint32_t vb = S.vaddr[db] + ST * TILE_B + h * 32 * ROWB + kc * 16 * ROWB;
-                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb));
-                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb + 4 * ROWB));
-                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-                vf[kc][db] = as_v8((u32x4_t){l2[0], l2[1], h2[0], h2[1]});
-            }
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) {
-                    const u32x4_t pp = {pk[qg][kc][0], pk[qg][kc][1], pk[qg][kc][2], pk[qg][kc][3]};
-                    S.acc[qg][db] = M::mma(vf[kc][db], as_v8(pp), S.acc[qg][db]);
+                for (int db = 0; db < DB; ++db) {
+                    const uint32_t vb = S.vaddr[db] + voff + h * 32 * ROWB + kc * 16 * ROWB;
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb));
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb + 4 * ROWB));
+                    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                    vf[h][kc][db] = as_v8((u32x4_t){l2[0], l2[1], h2[0], h2[1]});
                 }
+        s[0] = (f32x16_t){};
+        s[1] = (f32x16_t){};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) s[h] = M::mma(kf[h][cc], S.qf[cc], s[h]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const u32x4_t pp = {pk[h][kc][0], pk[h][kc][1], pk[h][kc][2], pk[h][kc][3]};
+                    S.acc[db] = M::mma(vf[h][kc][db], as_v8(pp), S.acc[db]);
+                }
+        // Issue order: a first batch of V^T reads, then each score MFMA followed by
+        // two more reads (a fragment is two transposing reads), then the P V MFMAs.
+        constexpr int NV = 8 * DB;       // transposing reads per unit
+        constexpr int NS = 2 * DC;       // score MFMAs per unit
+        constexpr int FIRST = kGemmFirstReads < NV ? kGemmFirstReads : NV;
+        constexpr int PER = (NV - FIRST + NS - 1) / NS;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST, 0);
+        sched_mfma_reads<NS, PER, NV - FIRST>();
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DB, 0);
     }
 
-    // is the key of accumulator register i of half h visible to row group qg of this lane?
-    static __device__ __forceinline__ bool visible(const State &S, int k0, int h, int qg, int i) {
+    // is the key of accumulator register i of half h visible to this lane's row?
+    static __device__ __forceinline__ bool visible(const State &S, int k0, int h, int i) {
         const int key = k0 + 32 * h + (i & 7) + 8 * S.g + 16 * (i >> 3);
-        return key < S.N && (!CAUSAL || key <= S.q0 + 32 * qg + S.l32);
+        return key < S.N && (!CAUSAL || key <= S.r0 + S.l32);
     }
 
-    // row max of a half in the log2 domain (-inf when nothing is visible)
+    // Softmax phase of the unit starting at key k0: row max, lazy move of the
+    // reference max (with the rescale of O^T and of the row sum), p = 2^(s c - m),
+    // P rounded to T in the B-operand layout, fp32 row sum of p.
     template <bool MASKED>
-    static __device__ __forceinline__ float row_max(const State &S, const f32x16_t &s, int k0, int h, int qg) {
+    static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, MASKED ? (visible(S, k0, h, qg, i) ? s[i] : -INFINITY) : s[i]);
-        mx = lane_swap32_max(mx);
-        return MASKED ? (mx == -INFINITY ? -INFINITY : mx * S.c) : mx * S.c;
-    }
-
-    // p = 2^(s c - m) in place
-    template <bool MASKED>
-    static __device__ __forceinline__ void exponentials(const State &S, f32x16_t &s, int k0, int h, int qg) {
-        const float nm = S.m_ref[qg] == -INFINITY ? 0.f : -S.m_ref[qg];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float p = fast_exp2(fmaf(s[i], S.c, nm));
-            if (MASKED) p = visible(S, k0, h, qg, i) ? p : 0.f;
-            s[i] = p;
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, MASKED ? (visible(S, k0, h, i) ? s[h][i] : -INFINITY) : s[h][i]);
+        mx = lane_swap32_max(mx);
+        const float mt = MASKED ? (mx == -INFINITY ? -INFINITY : mx * S.c) : mx * S.c;
+        if (__builtin_amdgcn_ballot_w64(mt > S.m_ref + TAU)) {
+            const float m_new = fmaxf(S.m_ref, mt);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
+            S.lsum *= alpha;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
+            S.m_ref = m_new;
         }
-    }
-
-    // round p to T in pairs (two 16-key B operands) and add the fp32 p to the row sum
-    static __device__ __forceinline__ void pack_sum(State &S, const f32x16_t &p, int qg, Packed &pk) {
+        const float nm = S.m_ref == -INFINITY ? 0.f : -S.m_ref;
         float rs = 0.f;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = p[8 * kc + 2 * e], p1 = p[8 * kc + 2 * e + 1];
-                pk[kc][e] = M::pack(p0, p1);
-                rs += p0 + p1;
-            }
-        S.lsum[qg] += rs;
-    }
-
-    // Move the reference max of group qg to mt; returns the factor applied.
-    static __device__ __forceinline__ float rescale(State &S, int qg, float mt) {
-        const float m_new = fmaxf(S.m_ref[qg], mt);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref[qg] - m_new);
-        S.lsum[qg] *= alpha;
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) S.acc[qg][b][i] *= alpha;
-        S.m_ref[qg] = m_new;
-        return alpha;
-    }
-
-    // One key tile for one wave, as two 32-key halves:
-    //   S(h0); max; [rescale];  exp(h0) | S(h1);  max; [rescale incl. pending p(h0)];
-    //   pack(h0) + exp(h1) | PV(h0);  pack(h1) | PV(h1)
-    template <bool MASKED, int ST>
-    static __device__ __forceinline__ void tile(State &S, int k0) {
-        sub<MASKED, ST, 0>(S, k0);
-        sub<MASKED, ST, 2>(S, k0 + 64);
-    }
-    // 64 keys of the tile: quarters Q0 and Q0 + 1
-    template <bool MASKED, int ST, int Q0>
-    static __device__ __forceinline__ void sub(State &S, int k0) {
-        f32x16_t s0[QG], s1[QG];
-        float mt[QG];
-        s_half<ST>(S, Q0, s0);
-        bool grow = false;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            mt[qg] = row_max<MASKED>(S, s0[qg], k0, 0, qg);
-            grow = grow || mt[qg] > S.m_ref[qg] + TAU;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) rescale(S, qg, mt[qg]);
-        }
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) exponentials<MASKED>(S, s0[qg], k0, 0, qg);
-        s_half<ST>(S, Q0 + 1, s1);
-        grow = false;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            mt[qg] = row_max<MASKED>(S, s1[qg], k0, 1, qg);
-            grow = grow || mt[qg] > S.m_ref[qg] + TAU;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                const float alpha = rescale(S, qg, mt[qg]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s0[qg][i] *= alpha;  // p(h0) joins the new reference
-            }
-        }
-        Packed pk0[QG], pk1[QG];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            pack_sum(S, s0[qg], qg, pk0[qg]);
-            exponentials<MASKED>(S, s1[qg], k0, 1, qg);
-        }
-        pv_half<ST>(S, Q0, pk0);
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) pack_sum(S, s1[qg], qg, pk1[qg]);
-        pv_half<ST>(S, Q0 + 1, pk1);
+                for (int e = 0; e < 4; ++e) {
+                    const int i0 = 8 * kc + 2 * e;
+                    float p0 = fast_exp2(fmaf(s[h][i0], S.c, nm));
+                    float p1 = fast_exp2(fmaf(s[h][i0 + 1], S.c, nm));
+                    if (MASKED) {
+                        p0 = visible(S, k0, h, i0) ? p0 : 0.f;
+                        p1 = visible(S, k0, h, i0 + 1) ? p1 : 0.f;
+                    }
+                    pk[h][kc][e] = M::pack(p0, p1);
+                    rs += p0 + p1;
+                }
+        S.lsum += rs;
     }
 
     // ------------------------------------------------------------ kernel body
+
+    // Workgroup barrier after this wave's DMA has at most VMCNT loads in flight and
+    // its LDS reads have completed; nothing is scheduled across it.
+    template <int VMCNT>
+    static __device__ __forceinline__ void barrier() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(VMCNT) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     static __device__ void run(const FwdArgs &a) {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -322,9 +326,12 @@ struct MfmaFwd {
         const int tid = threadIdx.x;
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
         const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+        // Waves w and w + 4 share a SIMD and form the two phase groups; they take
+        // neighbouring 32-row blocks so that both need the same number of key units.
+        const bool lag = w >= NW / 2;
 
         State S;
-        S.q0 = qt * BR + w * QG * 32;
+        S.r0 = qt * BR + 64 * (w & 3) + 32 * (w >> 2);
         S.N = N;
         S.l32 = l32;
         S.g = g;
@@ -336,26 +343,26 @@ struct MfmaFwd {
             qsign = 0x80008000u;
         }
 
-        // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its rows q
+        // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its row q
         // (rows past the end read row N-1 and are zeroed).
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            const int q = S.q0 + 32 * qg + l32;
+        {
+            const int q = S.r0 + l32;
             const uint32_t keep = q < N ? 0xffffffffu : 0u;
             const uint16_t *qrow = Qh + (size_t)min(q, N - 1) * D + g * 8;
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
                 u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + cc * 16);
                 x = (x & keep) ^ qsign;
-                S.qf[qg][cc] = as_v8(x);
+                S.qf[cc] = as_v8(x);
             }
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) S.acc[qg][b][i] = 0.f;
-            S.m_ref[qg] = -INFINITY;
-            S.lsum[qg] = 0.f;
         }
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S.acc[b][i] = 0.f;
+        S.m_ref = -INFINITY;
+        S.lsum = 0.f;
+
         // Fragment read addresses (stage 0; the stage, the key half and the key chunk
         // are added as immediate offsets).  K: lane reads chunk 2 cc + g of LDS row
         // l32, stored at chunk (2 cc + g) ^ kswz(l32).  V^T: 16-lane group grp reads
@@ -372,8 +379,8 @@ struct MfmaFwd {
             for (int db = 0; db < DB; ++db)
                 S.vaddr[db] = lds0 + V_BASE + r_lane * ROWB + (((4 * db + c_lane) ^ vswz(r_lane)) << 4) + 8 * (j16 & 1);
         }
-        // Tile loads: lane fills LDS slot s with chunk (slot ^ swizzle) of K row
-        // sigma(row) and of V row row.  Offsets are tile relative: row * ROWB + chunk * 16.
+        // Unit loads: lane fills LDS slot s with chunk (slot ^ swizzle) of K row
+        // sigma(row) and of V row row.  Offsets are unit relative: row * ROWB + chunk * 16.
         uint32_t kld[LOADS], vld[LOADS];
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
@@ -383,107 +390,153 @@ struct MfmaFwd {
             vld[i] = r * ROWB + ((p ^ vswz(r)) << 4);
         }
 
-        const int n_kv_all = (N + BC - 1) / BC;
-        const int n_kv = CAUSAL ? min(n_kv_all, (qt * BR + BR - 1) / BC + 1) : n_kv_all;
+        // Units of BU keys this workgroup and this wave need.
+        const int n_units = (N + BU - 1) / BU;
+        const int nu_wg = CAUSAL ? min(n_units, (min(qt * BR + BR, N) - 1) / BU + 1) : n_units;
+        const int nu = S.r0 >= N ? 0 : (CAUSAL ? min(n_units, (S.r0 + 31) / BU + 1) : n_units);
 
-        auto issue_loads = [&](int j) {
-            const int k0 = j * BC;
-            unsigned char *ks = smem + (j % STAGES) * TILE_B;
-            unsigned char *vs = smem + V_BASE + (j % STAGES) * TILE_B;
-            const char *kt = Kh + (size_t)k0 * ROWB;
-            const char *vt = Vh + (size_t)k0 * ROWB;
-            if (k0 + BC <= N) {
+        // DMA of one K or V unit into a ring stage.  Rows past the end of the sequence
+        // read row N - 1 (their scores are masked); the clamp is a no-op for full units.
+        auto load_unit = [&](const char *src_head, int lds_off, const uint32_t (&ld)[LOADS], int unit) {
+            const int k0 = unit * BU;
+            const char *src = src_head + (size_t)k0 * ROWB;
+            const uint32_t dst = lds0 + lds_off + w * LOADS * 1024;
+            const uint32_t last = (uint32_t)min(N - 1 - k0, BU - 1) * ROWB;
 #pragma unroll
-                for (int i = 0; i < LOADS; ++i) {
-                    __builtin_amdgcn_global_load_lds((const void *)(kt + kld[i]),
-                                                     (lds_void_t *)(ks + (w * LOADS + i) * 1024), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds((const void *)(vt + vld[i]),
-                                                     (lds_void_t *)(vs + (w * LOADS + i) * 1024), 16, 0, 0);
-                }
-            } else {  // last, partial tile: rows past the end read row N-1 (their scores are masked)
-                const uint32_t last = (uint32_t)(N - 1 - k0) * ROWB;
-#pragma unroll
-                for (int i = 0; i < LOADS; ++i) {
-                    const uint32_t kr = kld[i] & ~(uint32_t)(ROWB - 1), vr = vld[i] & ~(uint32_t)(ROWB - 1);
-                    const uint32_t ko = min(kr, last) + (kld[i] & (ROWB - 1));
-                    const uint32_t vo = min(vr, last) + (vld[i] & (ROWB - 1));
-                    __builtin_amdgcn_global_load_lds((const void *)(kt + ko),
-                                                     (lds_void_t *)(ks + (w * LOADS + i) * 1024), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds((const void *)(vt + vo),
-                                                     (lds_void_t *)(vs + (w * LOADS + i) * 1024), 16, 0, 0);
-                }
+            for (int i = 0; i < LOADS; ++i) {
+                const uint32_t off = min(ld[i] & ~(uint32_t)(ROWB - 1), last) + (ld[i] & (ROWB - 1));
+                dma_to_lds16(src, off, dst + i * 1024);
             }
         };
-        auto next = [&](int j) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();  // tile j is in LDS; every wave is done with tile j-1
-            if (j + 1 < n_kv) issue_loads(j + 1);
+        // Load group i (i >= 1): K of unit i into stage i mod STAGES and V of unit i - 1
+        // into stage (i - 1) mod STAGES.  Groups past the last unit repeat the last unit
+        // into stages nobody reads any more, so that every group is GROUP loads and
+        // the wait below is one constant count.
+        auto issue = [&](int i) {
+            load_unit(Kh, (i % STAGES) * UNIT_B, kld, min(i, nu_wg - 1));
+            load_unit(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld, min(i - 1, nu_wg - 1));
+        };
+        // Barriers wait for this wave's DMA.  Data of load group i is read from the
+        // barrier that ends the first group's matrix phase of unit i - 1 on (K fragments
+        // of unit i by the first group's softmax phase, V of unit i - 1 by the matrix
+        // phases of unit i).  Before a mid-step barrier a wave has issued groups up to
+        // u + STAGES - 1 and needs group u + 1; before the barrier that ends a step the
+        // lagging group needs group u + 2 (the first group needs less).
+        constexpr int MID = GROUP * (STAGES - 2), END = GROUP * (STAGES - 3);
+        auto barrier_mid = [&]() { barrier<MID>(); };
+        auto barrier_end = [&]() { barrier<END>(); };
+
+        // The matrix phase of unit 0 also runs the P V stream, with P = 0 against the
+        // V ring stage that unit -1 would use, zeroed here; the matrix phase of unit
+        // nu (P V of the wave's last unit) also computes scores it never uses.
+        f32x16_t s[2];
+        Packed pk;
+        KFrags kf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[h][kc][e] = 0u;
+        {
+            u32x4_t *vz = reinterpret_cast<u32x4_t *>(smem + V_BASE + (STAGES - 1) * UNIT_B);
+            for (int i = tid; i < UNIT_B / 16; i += THREADS) vz[i] = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+        // Steps u = 0 .. nu_wg.  A step is the matrix phase of unit u, a barrier, the
+        // softmax phase of unit u (which also reads the K fragments of unit u + 1), a
+        // barrier.  The lagging group runs one phase behind, so on every SIMD one wave
+        // issues MFMAs while the other computes exponentials; both groups pass the
+        // same barriers.  This wave computes in steps 0 .. nu (unit nu - 1 masked, step
+        // nu only finishes P V) and only loads in the rest.
+        auto pin_soft = [&]() {  // softmax results are complete before the barrier that ends their phase
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) asm volatile("" : "+v"(*reinterpret_cast<u32x4_t *>(pk[h][kc])));
+            asm volatile("" : "+v"(S.lsum), "+v"(S.m_ref));
+        };
+        auto plain_step = [&](auto st, int u) {
+            constexpr int ST = decltype(st)::value;  // u mod STAGES
+            issue(u + STAGES - 1);
+            gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B);
+            barrier_mid();
+            kload(S, kf, ((ST + 1) % STAGES) * UNIT_B);
+            soft<false>(S, s, pk, u * BU);
+            pin_soft();
+            barrier_end();
         };
 
-        // Tiles [0, j_plain) are fully visible to every row of this wave; the rest
-        // cross its diagonal, hold the end of the sequence, or (causal) lie wholly
-        // after its rows and are skipped.  Two loops keep one tile body per loop.
-        const int j_plain = min(n_kv, min(CAUSAL ? (S.q0 + 1) / BC : n_kv, N / BC));
-        issue_loads(0);
-        int j = 0;
-        // (unrolled by two so the LDS stage of each tile is a compile-time offset)
-        for (; j + 1 < j_plain; j += 2) {
-            next(j);
-            tile<false, 0>(S, j * BC);
-            next(j + 1);
-            tile<false, 1>(S, (j + 1) * BC);
+        // prologue: group 0 is K of unit 0 only (V stage STAGES - 1 holds zeros)
+        load_unit(Kh, 0, kld, 0);
+        for (int i = 1; i < STAGES - 1; ++i) issue(i);
+        barrier_mid();
+        kload(S, kf, 0);
+        if (lag) barrier_end();
+        int u = 0;
+        // steps whose softmax needs no mask: u < nu - 1, unrolled so the ring stage is an immediate
+        for (; u + STAGES < nu; u += STAGES) {
+            plain_step(std::integral_constant<int, 0>(), u);
+            plain_step(std::integral_constant<int, 1>(), u + 1);
+            plain_step(std::integral_constant<int, 2>(), u + 2);
+            plain_step(std::integral_constant<int, 3>(), u + 3);
         }
-        if (j < j_plain) {
-            next(j);
-            tile<false, 0>(S, j * BC);  // j is even here
-            ++j;
+        for (; u + 1 < nu; ++u) {  // remaining plain steps, ring stage from u
+            issue(u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            barrier_mid();
+            kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
+            soft<false>(S, s, pk, u * BU);
+            pin_soft();
+            barrier_end();
         }
-        for (; j < n_kv; ++j) {
-            next(j);
-            const int k0 = j * BC;
-            if (CAUSAL && k0 > S.q0 + QG * 32 - 1) continue;  // every key after every row of this wave
-            if (j & 1)
-                tile<true, 1>(S, k0);
-            else
-                tile<true, 0>(S, k0);
+        if (nu > 0) {  // step nu - 1 (masked softmax) and step nu (P V of the last unit)
+            issue(u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            barrier_mid();
+            kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
+            soft<true>(S, s, pk, u * BU);
+            pin_soft();
+            barrier_end();
+            ++u;
+            issue(u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            barrier_mid();
+            barrier_end();
+            ++u;
         }
+        for (; u <= nu_wg; ++u) {  // steps after this wave's last unit: loads and barriers only
+            issue(u + STAGES - 1);
+            barrier_mid();
+            barrier_end();
+        }
+        if (!lag) barrier<0>();
 
         // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
         // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q.
+        const int q = S.r0 + l32;
+        const float ltot = lane_swap32_add(S.lsum);
+        if (q < N) {
+            const float inv = 1.f / ltot;
+            uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            const int q = S.q0 + 32 * qg + l32;
-            const float ltot = lane_swap32_add(S.lsum[qg]);
-            if (q < N) {
-                const float inv = 1.f / ltot;
-                uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
+            for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int quad = 0; quad < 4; ++quad) {
-                        const uint32_t lo = M::pack(S.acc[qg][b][quad * 4 + 0] * inv, S.acc[qg][b][quad * 4 + 1] * inv);
-                        const uint32_t hi = M::pack(S.acc[qg][b][quad * 4 + 2] * inv, S.acc[qg][b][quad * 4 + 3] * inv);
-                        const u32x2_t y = {lo, hi};
-                        *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
-                    }
-                if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref[qg] + fast_log2(ltot)) * kLn2;
-            }
+                for (int quad = 0; quad < 4; ++quad) {
+                    const uint32_t lo = M::pack(S.acc[b][quad * 4 + 0] * inv, S.acc[b][quad * 4 + 1] * inv);
+                    const uint32_t hi = M::pack(S.acc[b][quad * 4 + 2] * inv, S.acc[b][quad * 4 + 3] * inv);
+                    const u32x2_t y = {lo, hi};
+                    *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
+                }
+            if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
         }
     }
 };
 
-// Rows per wave: 32 (one group, two waves per SIMD).  The kernel also builds
-// with two groups (64 rows, one wave per SIMD, half the LDS bytes per MFMA
-// flop); on gfx950 that measured slower (820 vs 930 TFLOP/s on the causal
-// N=8192 d=128 workload) because the compiler then moves the O accumulators
-// between register files.
-constexpr int kRowGroups = 1;
-
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512 / kRowGroups, 1)
+__global__ __launch_bounds__(512, 1)
 void attn_fwd_mfma_kernel(FwdArgs a) {
-    static_assert(MfmaFwd<T, D, CAUSAL, kRowGroups>::THREADS == 512 / kRowGroups, "launch bounds");
-    MfmaFwd<T, D, CAUSAL, kRowGroups>::run(a);
+    static_assert(MfmaFwd<T, D, CAUSAL>::THREADS == 512, "launch bounds");
+    MfmaFwd<T, D, CAUSAL>::run(a);
 }
 
 }  // namespace attn
