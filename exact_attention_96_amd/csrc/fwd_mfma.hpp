@@ -314,10 +314,24 @@ struct MfmaFwd {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
         const int N = a.N;
-        const int logical = xcd_contiguous(blockIdx.x, a.total);
-        const int bh = logical / a.n_qtiles;
-        const int t_ = logical - bh * a.n_qtiles;
-        const int qt = CAUSAL ? a.n_qtiles - 1 - t_ : t_;  // causal: longest rows first
+        // Work order.  Causal: the block index is the rank in a longest-first order
+        // (query tiles from the last to the first, all heads for each), so the
+        // dispatcher always starts the longest remaining tile and the 8 XCDs, which
+        // take block indices round robin, receive equal shares (and, when B*H is a
+        // multiple of 8, always the same heads).  Non-causal tiles are all equal:
+        // each XCD takes a contiguous range of (head, tile) pairs, so consecutive
+        // tiles of a head share its L2.
+        int logical, bh, qt;
+        if (CAUSAL) {
+            const int n_bh = a.total / a.n_qtiles;
+            logical = blockIdx.x;
+            bh = logical % n_bh;
+            qt = a.n_qtiles - 1 - logical / n_bh;
+        } else {
+            logical = xcd_contiguous(blockIdx.x, a.total);
+            bh = logical / a.n_qtiles;
+            qt = logical - bh * a.n_qtiles;
+        }
         const size_t head = (size_t)bh * (size_t)N * D;
         const uint16_t *Qh = static_cast<const uint16_t *>(a.q) + head;
         const char *Kh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head);
