@@ -524,6 +524,9 @@ struct MfmaFwd {
             barrier_end();
         }
         if (!lag) barrier<0>();
+        // Every DMA of this wave has landed before it leaves: the LDS it writes belongs
+        // to this workgroup only while the workgroup runs.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
         // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q.
