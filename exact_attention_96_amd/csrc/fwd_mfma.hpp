@@ -40,14 +40,17 @@
 // is a per-lane multiply.  The V^T A operand comes from the row-major V unit
 // through ds_read_b64_tr_b16 (each 16-lane group transposes a 4 x 16 block).
 //
-// Softmax arithmetic.  t = s * c with c = scale * log2(e); p = 2^(t - m).
-// The reference m is only moved when a row max exceeds it by more than
-// TAU = 8 (in log2 units), so the O rescale runs a handful of times per row
-// instead of once per unit.  This changes no result: softmax is invariant to
-// the shift (same page, "数值稳定的 Softmax"), and p <= 2^8 keeps every
-// intermediate far inside fp32/bf16/fp16 range.  The row sum adds the fp32
-// probabilities before their rounding to the input type, so lse keeps fp32
-// accuracy (a sum of bf16-rounded terms would cost ~2^-9 relative in l).
+// Softmax arithmetic.  t = s * c with c = scale * log2(e); p = 2^(t - m) against
+// a reference m that only moves when needed: each lane adds its 32 fp32 values
+// of p for the unit, and that sum bounds every one of them, so while no lane's
+// sum exceeds 2^16 the values are in range and no row max is computed at all.
+// Otherwise (the first unit, or a row whose max grew well past m) the unit's row
+// max is taken, m moves to it, O~ and the row sum are rescaled and p is recomputed.
+// This changes no result: softmax is invariant to the shift (same page,
+// "数值稳定的 Softmax"), and p <= 2^16 keeps every intermediate far inside
+// fp32/bf16/fp16 range.  The row sum adds the fp32 probabilities before their
+// rounding to the input type, so lse keeps fp32 accuracy (a sum of bf16-rounded
+// terms would cost ~2^-9 relative in l).
 #pragma once
 
 #include <type_traits>
@@ -163,7 +166,7 @@ struct MfmaFwd {
     static constexpr int GROUP = 2 * LOADS;          // DMA loads per wave in one load group
     static constexpr int DB = D / 32;                // 32-row blocks of O^T
     static constexpr int DC = D / 16;                // k-steps of the first product
-    static constexpr float TAU = 8.0f;
+    static constexpr float kSumBound = 65536.0f;  // 2^SUM_LOG2 with SUM_LOG2 = 16
     static_assert(LOADS >= 1 && LOADS * 64 * NW == BU * CH, "unit loads split evenly over the waves");
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
     static_assert(STAGES >= 3, "waits assume at least three ring stages");
@@ -207,9 +210,13 @@ struct MfmaFwd {
     // Matrix phase: S^T of unit u (K fragments already in registers) and
     // O^T += V^T P^T of unit u - 1 (V in ring stage offset voff, P from the previous
     // softmax phase).  The V^T reads are issued first; the score MFMAs, which need no
-    // LDS data, run while they are in flight.
+    // LDS data, run while they are in flight.  dma(j) issues load j of this step's
+    // load group; the loads go one per quarter of the P V MFMAs, each right after an
+    // MFMA, so that a load waiting for the CU's vector-memory pipe (busy with the
+    // other waves' loads) delays no MFMA.
+    template <typename Dma>
     static __device__ __forceinline__ void gemm(State &S, f32x16_t (&s)[2], const Packed &pk, const KFrags &kf,
-                                                uint32_t voff) {
+                                                uint32_t voff, Dma &&dma) {
         v8 vf[2][2][DB];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -229,24 +236,29 @@ struct MfmaFwd {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) s[h] = M::mma(kf[h][cc], S.qf[cc], s[h]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const u32x4_t pp = {pk[h][kc][0], pk[h][kc][1], pk[h][kc][2], pk[h][kc][3]};
-                    S.acc[db] = M::mma(vf[h][kc][db], as_v8(pp), S.acc[db]);
-                }
         // Issue order: a first batch of V^T reads, then each score MFMA followed by
-        // two more reads (a fragment is two transposing reads), then the P V MFMAs.
+        // two more reads (a fragment is two transposing reads).
         constexpr int NV = 8 * DB;       // transposing reads per unit
         constexpr int NS = 2 * DC;       // score MFMAs per unit
         constexpr int FIRST = kGemmFirstReads < NV ? kGemmFirstReads : NV;
         constexpr int PER = (NV - FIRST + NS - 1) / NS;
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST, 0);
         sched_mfma_reads<NS, PER, NV - FIRST>();
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DB, 0);
+        constexpr int NP = 4 * DB;       // P V MFMAs per unit
+        constexpr int CHUNK = NP / GROUP;
+        static_assert(NP % GROUP == 0, "P V MFMAs split evenly around the loads");
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int h = j / (2 * DB), kc = (j / DB) % 2, db = j % DB;
+            const u32x4_t pp = {pk[h][kc][0], pk[h][kc][1], pk[h][kc][2], pk[h][kc][3]};
+            __builtin_amdgcn_sched_barrier(0);
+            S.acc[db] = M::mma(vf[h][kc][db], as_v8(pp), S.acc[db]);
+            if (j % CHUNK == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma(j / CHUNK);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // is the key of accumulator register i of half h visible to this lane's row?
@@ -255,29 +267,10 @@ struct MfmaFwd {
         return key < S.N && (!CAUSAL || key <= S.r0 + S.l32);
     }
 
-    // Softmax phase of the unit starting at key k0: row max, lazy move of the
-    // reference max (with the rescale of O^T and of the row sum), p = 2^(s c - m),
-    // P rounded to T in the B-operand layout, fp32 row sum of p.
+    // p = 2^(s c - m) for the unit starting at key k0 against the current reference
+    // m, rounded to T in the B-operand layout; returns this lane's fp32 sum of p.
     template <bool MASKED>
-    static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, MASKED ? (visible(S, k0, h, i) ? s[h][i] : -INFINITY) : s[h][i]);
-        mx = lane_swap32_max(mx);
-        const float mt = MASKED ? (mx == -INFINITY ? -INFINITY : mx * S.c) : mx * S.c;
-        if (__builtin_amdgcn_ballot_w64(mt > S.m_ref + TAU)) {
-            const float m_new = fmaxf(S.m_ref, mt);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
-            S.lsum *= alpha;
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
-            S.m_ref = m_new;
-        }
+    static __device__ __forceinline__ float exps(const State &S, const f32x16_t (&s)[2], Packed &pk, int k0) {
         const float nm = S.m_ref == -INFINITY ? 0.f : -S.m_ref;
         float rs = 0.f;
 #pragma unroll
@@ -296,6 +289,37 @@ struct MfmaFwd {
                     pk[h][kc][e] = M::pack(p0, p1);
                     rs += p0 + p1;
                 }
+        return rs;
+    }
+
+    // Softmax phase of the unit starting at key k0.  The exponentials are taken
+    // against the current reference m first; the lane's fp32 sum of its 32 values
+    // bounds each of them, so when no lane's sum exceeds 2^SUM_LOG2 every p is in
+    // range and the unit is done.  Otherwise (the first unit, or a row whose max has
+    // grown well past m) the row max of the unit is taken, m moves to it, O~ and the
+    // row sum are rescaled, and the exponentials are taken again.
+    template <bool MASKED>
+    static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0) {
+        float rs = exps<MASKED>(S, s, pk, k0);
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound) || S.m_ref == -INFINITY)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, MASKED ? (visible(S, k0, h, i) ? s[h][i] : -INFINITY) : s[h][i]);
+            mx = lane_swap32_max(mx);
+            const float mt = mx == -INFINITY ? -INFINITY : mx * S.c;
+            const float m_new = fmaxf(S.m_ref, mt);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
+            S.lsum *= alpha;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
+            S.m_ref = m_new;
+            rs = exps<MASKED>(S, s, pk, k0);
+        }
         S.lsum += rs;
     }
 
@@ -409,27 +433,37 @@ struct MfmaFwd {
         const int nu_wg = CAUSAL ? min(n_units, (min(qt * BR + BR, N) - 1) / BU + 1) : n_units;
         const int nu = S.r0 >= N ? 0 : (CAUSAL ? min(n_units, (S.r0 + 31) / BU + 1) : n_units);
 
-        // DMA of one K or V unit into a ring stage.  Rows past the end of the sequence
-        // read row N - 1 (their scores are masked); the clamp is a no-op for full units.
-        auto load_unit = [&](const char *src_head, int lds_off, const uint32_t (&ld)[LOADS], int unit) {
+        // Load j of a unit (16 bytes per lane) into a ring stage.  Rows past the end of
+        // the sequence read row N - 1 (their scores are masked); the clamp is a no-op
+        // for full units.
+        auto load_one = [&](const char *src_head, int lds_off, uint32_t ld, int unit, int j) {
             const int k0 = unit * BU;
             const char *src = src_head + (size_t)k0 * ROWB;
-            const uint32_t dst = lds0 + lds_off + w * LOADS * 1024;
+            const uint32_t dst = lds0 + lds_off + (w * LOADS + j) * 1024;
             const uint32_t last = (uint32_t)min(N - 1 - k0, BU - 1) * ROWB;
+            const uint32_t off = min(ld & ~(uint32_t)(ROWB - 1), last) + (ld & (ROWB - 1));
+            dma_to_lds16(src, off, dst);
+        };
+        auto load_unit = [&](const char *src_head, int lds_off, const uint32_t (&ld)[LOADS], int unit) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const uint32_t off = min(ld[i] & ~(uint32_t)(ROWB - 1), last) + (ld[i] & (ROWB - 1));
-                dma_to_lds16(src, off, dst + i * 1024);
-            }
+            for (int j = 0; j < LOADS; ++j) load_one(src_head, lds_off, ld[j], unit, j);
         };
         // Load group i (i >= 1): K of unit i into stage i mod STAGES and V of unit i - 1
         // into stage (i - 1) mod STAGES.  Groups past the last unit repeat the last unit
         // into stages nobody reads any more, so that every group is GROUP loads and
-        // the wait below is one constant count.
-        auto issue = [&](int i) {
-            load_unit(Kh, (i % STAGES) * UNIT_B, kld, min(i, nu_wg - 1));
-            load_unit(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld, min(i - 1, nu_wg - 1));
+        // the waits below are constant counts.  issue_part(i, j) issues load j of the
+        // group (K loads first, then V loads).
+        auto issue_part = [&](int i, int j) {
+            if (j < LOADS)
+                load_one(Kh, (i % STAGES) * UNIT_B, kld[j], min(i, nu_wg - 1), j);
+            else
+                load_one(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld[j - LOADS], min(i - 1, nu_wg - 1), j - LOADS);
         };
+        auto issue = [&](int i) {
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) issue_part(i, j);
+        };
+
         // Barriers wait for this wave's DMA.  Data of load group i is read from the
         // barrier that ends the first group's matrix phase of unit i - 1 on (K fragments
         // of unit i by the first group's softmax phase, V of unit i - 1 by the matrix
@@ -471,8 +505,7 @@ struct MfmaFwd {
         };
         auto plain_step = [&](auto st, int u) {
             constexpr int ST = decltype(st)::value;  // u mod STAGES
-            issue(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B);
+            gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((ST + 1) % STAGES) * UNIT_B);
             soft<false>(S, s, pk, u * BU);
@@ -495,8 +528,7 @@ struct MfmaFwd {
             plain_step(std::integral_constant<int, 3>(), u + 3);
         }
         for (; u + 1 < nu; ++u) {  // remaining plain steps, ring stage from u
-            issue(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
             soft<false>(S, s, pk, u * BU);
@@ -504,16 +536,14 @@ struct MfmaFwd {
             barrier_end();
         }
         if (nu > 0) {  // step nu - 1 (masked softmax) and step nu (P V of the last unit)
-            issue(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
             soft<true>(S, s, pk, u * BU);
             pin_soft();
             barrier_end();
             ++u;
-            issue(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             barrier_end();
             ++u;
