@@ -261,10 +261,14 @@ struct MfmaFwd {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // is the key of accumulator register i of half h visible to this lane's row?
-    static __device__ __forceinline__ bool visible(const State &S, int k0, int h, int i) {
-        const int key = k0 + 32 * h + (i & 7) + 8 * S.g + 16 * (i >> 3);
-        return key < S.N && (!CAUSAL || key <= S.r0 + S.l32);
+    // Keys of a unit are visible to this lane's row up to a per-lane limit:
+    // accumulator register i of half h holds the key at offset key_off(h, i) from
+    // the unit start k0, and that key is visible iff key_off(h, i) <= lim(k0), with
+    // lim = min(row, N - 1) - k0 - 8 g (causal) or N - 1 - k0 - 8 g.
+    static __device__ __forceinline__ constexpr int key_off(int h, int i) { return 32 * h + (i & 7) + 16 * (i >> 3); }
+    static __device__ __forceinline__ int vis_limit(const State &S, int k0) {
+        const int last = CAUSAL ? min(S.r0 + S.l32, S.N - 1) : S.N - 1;
+        return last - k0 - 8 * S.g;
     }
 
     // p = 2^(s c - m) for the unit starting at key k0 against the current reference
@@ -272,6 +276,7 @@ struct MfmaFwd {
     template <bool MASKED>
     static __device__ __forceinline__ float exps(const State &S, const f32x16_t (&s)[2], Packed &pk, int k0) {
         const float nm = S.m_ref == -INFINITY ? 0.f : -S.m_ref;
+        const int lim = MASKED ? vis_limit(S, k0) : 0;
         float rs = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -283,8 +288,8 @@ struct MfmaFwd {
                     float p0 = fast_exp2(fmaf(s[h][i0], S.c, nm));
                     float p1 = fast_exp2(fmaf(s[h][i0 + 1], S.c, nm));
                     if (MASKED) {
-                        p0 = visible(S, k0, h, i0) ? p0 : 0.f;
-                        p1 = visible(S, k0, h, i0 + 1) ? p1 : 0.f;
+                        p0 = key_off(h, i0) <= lim ? p0 : 0.f;
+                        p1 = key_off(h, i0 + 1) <= lim ? p1 : 0.f;
                     }
                     pk[h][kc][e] = M::pack(p0, p1);
                     rs += p0 + p1;
@@ -294,31 +299,44 @@ struct MfmaFwd {
 
     // Softmax phase of the unit starting at key k0.  The exponentials are taken
     // against the current reference m first; the lane's fp32 sum of its 32 values
-    // bounds each of them, so when no lane's sum exceeds 2^SUM_LOG2 every p is in
-    // range and the unit is done.  Otherwise (the first unit, or a row whose max has
-    // grown well past m) the row max of the unit is taken, m moves to it, O~ and the
-    // row sum are rescaled, and the exponentials are taken again.
-    template <bool MASKED>
+    // bounds each of them, so when no lane's sum exceeds kSumBound every p is in
+    // range and the unit is done.  Otherwise (a row whose max grew well past m) the
+    // row max of the unit is taken, m moves to it, O~ and the row sum are rescaled,
+    // and the exponentials are taken again.  The first unit of a tile (FIRST: m is
+    // still -inf, O~ and the sum are zero) starts from its row max directly.
+    template <bool MASKED, bool FIRST>
     static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0) {
-        float rs = exps<MASKED>(S, s, pk, k0);
-        if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound) || S.m_ref == -INFINITY)) {
+        auto move_reference = [&](bool rescale) {
+            const int lim = MASKED ? vis_limit(S, k0) : 0;
             float mx = -INFINITY;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, MASKED ? (visible(S, k0, h, i) ? s[h][i] : -INFINITY) : s[h][i]);
+                    mx = fmaxf(mx, MASKED ? (key_off(h, i) <= lim ? s[h][i] : -INFINITY) : s[h][i]);
             mx = lane_swap32_max(mx);
             const float mt = mx == -INFINITY ? -INFINITY : mx * S.c;
             const float m_new = fmaxf(S.m_ref, mt);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
-            S.lsum *= alpha;
+            if (rescale) {
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(S.m_ref - m_new);
+                S.lsum *= alpha;
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+                for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
+                    for (int i = 0; i < 16; ++i) S.acc[b][i] *= alpha;
+            }
             S.m_ref = m_new;
+        };
+        float rs;
+        if (FIRST) {
+            move_reference(false);
             rs = exps<MASKED>(S, s, pk, k0);
+        } else {
+            rs = exps<MASKED>(S, s, pk, k0);
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
+                move_reference(true);
+                rs = exps<MASKED>(S, s, pk, k0);
+            }
         }
         S.lsum += rs;
     }
@@ -508,7 +526,7 @@ struct MfmaFwd {
             gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((ST + 1) % STAGES) * UNIT_B);
-            soft<false>(S, s, pk, u * BU);
+            soft<false, false>(S, s, pk, u * BU);
             pin_soft();
             barrier_end();
         };
@@ -520,26 +538,39 @@ struct MfmaFwd {
         kload(S, kf, 0);
         if (lag) barrier_end();
         int u = 0;
-        // steps whose softmax needs no mask: u < nu - 1, unrolled so the ring stage is an immediate
-        for (; u + STAGES < nu; u += STAGES) {
-            plain_step(std::integral_constant<int, 0>(), u);
-            plain_step(std::integral_constant<int, 1>(), u + 1);
-            plain_step(std::integral_constant<int, 2>(), u + 2);
-            plain_step(std::integral_constant<int, 3>(), u + 3);
-        }
-        for (; u + 1 < nu; ++u) {  // remaining plain steps, ring stage from u
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+        if (nu > 1) {
+            // unit 0 (plain, first of the tile), then the plain units up to nu - 2,
+            // unrolled by four from unit 1 so that the ring stage is an immediate
+            gemm(S, s, pk, kf, (STAGES - 1) * UNIT_B, [&](int j) { issue_part(STAGES - 1, j); });
             barrier_mid();
-            kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
-            soft<false>(S, s, pk, u * BU);
+            kload(S, kf, 1 * UNIT_B);
+            soft<false, true>(S, s, pk, 0);
             pin_soft();
             barrier_end();
+            u = 1;
+            for (; u + STAGES < nu; u += STAGES) {
+                plain_step(std::integral_constant<int, 1>(), u);
+                plain_step(std::integral_constant<int, 2>(), u + 1);
+                plain_step(std::integral_constant<int, 3>(), u + 2);
+                plain_step(std::integral_constant<int, 0>(), u + 3);
+            }
+            for (; u + 1 < nu; ++u) {  // remaining plain steps, ring stage from u
+                gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+                barrier_mid();
+                kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
+                soft<false, false>(S, s, pk, u * BU);
+                pin_soft();
+                barrier_end();
+            }
         }
         if (nu > 0) {  // step nu - 1 (masked softmax) and step nu (P V of the last unit)
             gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
-            soft<true>(S, s, pk, u * BU);
+            if (u == 0)
+                soft<true, true>(S, s, pk, u * BU);
+            else
+                soft<true, false>(S, s, pk, u * BU);
             pin_soft();
             barrier_end();
             ++u;
