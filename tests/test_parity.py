@@ -109,6 +109,25 @@ def test_scale_values(dtype):
             full_parity(q, k, v, causal, scale, dtype, f"scale={scale}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_max_moves(dtype, d, causal):
+    """Scores that climb along the sequence by hundreds of log2 units (key norms grow
+    30x at scale 1): the matrix-core kernel's reference max must move, with a rescale of
+    the running output and sum, many times per row, also inside the masked diagonal
+    unit.  And the same keys in reverse order: the first unit holds every row's max.
+    (16-bit inputs only: that reference logic exists only in the matrix-core kernel;
+    fp32 inputs of this size are dominated by fp32 rounding of scores of ~300, above
+    the fp32 bar written for scores of ordinary size.)"""
+    B, H, N = 1, 2, 777
+    q, k, v = random_qkv(B, H, N, d, dtype, seed=31)
+    ramp = torch.linspace(0.2, 6.0, N, dtype=torch.float32)
+    for name, f in (("rising", ramp), ("falling", ramp.flip(0))):
+        kk = (k.float() * f[None, None, :, None]).to(k.dtype)
+        full_parity(q, kk, v, causal, 1.0, dtype, f"{name} scores d={d}")
+
+
 # ------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
