@@ -356,21 +356,30 @@ struct MfmaFwd {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
         const int N = a.N;
-        // Work order.  Causal: the block index is the rank in a longest-first order
-        // (query tiles from the last to the first, all heads for each), so the
-        // dispatcher always starts the longest remaining tile and the 8 XCDs, which
-        // take block indices round robin, receive equal shares (and, when B*H is a
-        // multiple of 8, always the same heads).  Non-causal tiles are all equal:
-        // each XCD takes a contiguous range of (head, tile) pairs, so consecutive
-        // tiles of a head share its L2.
-        int logical, bh, qt;
+        // Work order.  The 8 XCDs take block indices round robin, each with its own L2.
+        // Causal: longest tiles first, so that the dispatcher always starts the longest
+        // remaining tile.  When B*H is a multiple of 16, XCD x serves the heads congruent
+        // to x mod 8, a few at a time: groups of hg heads, each group's tiles from the
+        // last (longest) to the first, the heads of a group interleaved.  Tiles of one
+        // head then start close together and read its K and V units from the L2 at
+        // nearly the same time.  Otherwise the rank is simply longest-first over all
+        // heads.  Non-causal tiles are all equal: each XCD takes a contiguous range of
+        // (head, tile) pairs, so consecutive tiles of a head share its L2.
+        int bh, qt;
         if (CAUSAL) {
-            const int n_bh = a.total / a.n_qtiles;
-            logical = blockIdx.x;
-            bh = logical % n_bh;
-            qt = a.n_qtiles - 1 - logical / n_bh;
+            const int nq = a.n_qtiles, n_bh = a.total / nq, per = n_bh >> 3;
+            if ((n_bh & 15) == 0) {
+                const int hg = (per & 3) == 0 ? 4 : 2;
+                const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+                const int grp = j / (hg * nq), rem = j - grp * (hg * nq);
+                qt = nq - 1 - rem / hg;
+                bh = x + 8 * (grp * hg + rem % hg);
+            } else {
+                bh = blockIdx.x % n_bh;
+                qt = nq - 1 - blockIdx.x / n_bh;
+            }
         } else {
-            logical = xcd_contiguous(blockIdx.x, a.total);
+            const int logical = xcd_contiguous(blockIdx.x, a.total);
             bh = logical / a.n_qtiles;
             qt = logical - bh * a.n_qtiles;
         }

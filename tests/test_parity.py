@@ -94,6 +94,14 @@ def test_ragged_lengths(dtype, d, causal):
         full_parity(q, k, v, causal, 1.0 / math.sqrt(d), dtype, f"ragged N={N}")
 
 
+@pytest.mark.parametrize("B,H", [(2, 8), (1, 32), (4, 12)])
+def test_causal_tile_orders(B, H):
+    """Head counts that select each causal tile order of the matrix-core kernel
+    (16, 32 and 48 heads: groups of 2, 4 and 2 heads per XCD), with a ragged tail."""
+    q, k, v = random_qkv(B, H, 700, 128, "bf16", seed=40 + H)
+    full_parity(q, k, v, True, 1.0 / math.sqrt(128), "bf16", f"B={B} H={H} N=700")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_many_heads_short(dtype):
     q, k, v = random_qkv(8, 40, 96, 64, dtype, seed=7)
