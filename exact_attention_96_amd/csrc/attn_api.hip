@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fwd_f32.hpp"
 #include "fwd_mfma.hpp"
 
@@ -20,15 +22,39 @@ bool overlaps(const void *p, uint64_t n, const void *r, uint64_t m) {
     return a0 < b0 + m && b0 < a0 + n;
 }
 
+// Launch with the single kernel argument; returns this launch's own status (not an
+// error left behind by an earlier call).
+template <typename Kernel>
+hipError_t launch(Kernel *kernel, int grid, int threads, int lds_bytes, hipStream_t stream, FwdArgs args) {
+    void *argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3(grid), dim3(threads), argv,
+                           static_cast<size_t>(lds_bytes), stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32(const FwdArgs &a, int bh, hipStream_t stream) {
     constexpr int QW = attn::F32Fwd<D, CAUSAL>::QW;
     FwdArgs b = a;
     b.n_qtiles = (a.N + QW - 1) / QW;
     b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
-    hipLaunchKernelGGL((attn::attn_fwd_f32_kernel<D, CAUSAL>), dim3(b.total),
-                       dim3(attn::F32Fwd<D, CAUSAL>::THREADS), 0, stream, b);
-    return hipGetLastError();
+    return launch(&attn::attn_fwd_f32_kernel<D, CAUSAL>, b.total, attn::F32Fwd<D, CAUSAL>::THREADS, 0, stream, b);
+}
+
+// Opt the kernel in to its dynamic LDS size, once per device (devices 0..63; others
+// every call).
+template <typename T, int D, bool CAUSAL>
+hipError_t opt_in_lds(int lds_bytes) {
+    static std::atomic<uint64_t> done{0};
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < 64;
+    if (tracked && ((done.load(std::memory_order_acquire) >> dev) & 1u)) return hipSuccess;
+    const hipError_t r = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (r == hipSuccess && tracked) done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
+    return r;
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -38,14 +64,9 @@ hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
     b.n_qtiles = (a.N + K::BR - 1) / K::BR;
     b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
     constexpr int lds_bytes = K::LDS_B;
-    // opt in to the LDS size once per kernel (thread-safe static initialisation)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    const hipError_t attr = opt_in_lds<T, D, CAUSAL>(lds_bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn::attn_fwd_mfma_kernel<T, D, CAUSAL>), dim3(b.total), dim3(K::THREADS),
-                       lds_bytes, stream, b);
-    return hipGetLastError();
+    return launch(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>, b.total, K::THREADS, lds_bytes, stream, b);
 }
 
 template <int D, bool CAUSAL>

@@ -75,9 +75,10 @@ typedef enum {
  * input are bitwise reproducible from call to call.
  *
  * Ownership and concurrency: all buffers belong to the caller.  The library
- * allocates no memory and keeps no mutable state, so calls on different
- * streams or host threads may run concurrently.  o and lse must not overlap
- * q, k, v or each other.
+ * allocates no memory; its only mutable state is a per-device flag recording
+ * that the matrix-core kernels were opted in to their LDS size (set once,
+ * atomically), so calls on different streams or host threads may run
+ * concurrently.  o and lse must not overlap q, k, v or each other.
  *
  * Errors are returned synchronously and nothing is launched on error:
  *   ATTN_EINVAL       a NULL pointer; B, H or N < 1; d < 1; unknown dtype;
@@ -86,7 +87,8 @@ typedef enum {
  *                     q, k, v or each other.
  *   ATTN_EUNSUPPORTED d not 64 or 128; a problem whose tile count exceeds the
  *                     launch grid.
- *   ATTN_EHIP         the launch failed (hipGetLastError).
+ *   ATTN_EHIP         the launch itself failed (status of hipLaunchKernel or of
+ *                     the LDS opt-in, not an error left by an earlier call).
  * The call is asynchronous: results are valid once `stream` has completed.
  */
 ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
