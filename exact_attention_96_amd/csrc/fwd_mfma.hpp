@@ -599,23 +599,39 @@ struct MfmaFwd {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
-        // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q.
+        // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q, so the two lane halves
+        // of a row hold alternate groups of 4 columns.  One exchange between them (lane ^ 32,
+        // same row) gives every lane 8 consecutive columns: 16-byte stores, half as many
+        // store instructions as storing each lane's own groups of 4.
         const int q = S.r0 + l32;
         const float ltot = lane_swap32_add(S.lsum);
-        if (q < N) {
-            const float inv = 1.f / ltot;
-            uint16_t *Oh = static_cast<uint16_t *>(a.o) + head + (size_t)q * D;
+        const float inv = 1.f / ltot;
+        auto partner = [&](uint32_t x) -> uint32_t {  // x of lane ^ 32
+            const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            return g ? r[0] : r[1];
+        };
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int quad = 0; quad < 4; ++quad) {
-                    const uint32_t lo = M::pack(S.acc[b][quad * 4 + 0] * inv, S.acc[b][quad * 4 + 1] * inv);
-                    const uint32_t hi = M::pack(S.acc[b][quad * 4 + 2] * inv, S.acc[b][quad * 4 + 3] * inv);
-                    const u32x2_t y = {lo, hi};
-                    *reinterpret_cast<u32x2_t *>(Oh + b * 32 + quad * 8 + 4 * g) = y;
+            for (int k = 0; k < 4; k += 2) {  // column groups 8 k .. 8 k + 15 of block b
+                u32x2_t mine[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int i = 4 * (k + t);
+                    mine[t][0] = M::pack(S.acc[b][i + 0] * inv, S.acc[b][i + 1] * inv);
+                    mine[t][1] = M::pack(S.acc[b][i + 2] * inv, S.acc[b][i + 3] * inv);
                 }
-            if (g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
-        }
+                // lane half 0 keeps group k and receives the other half's group k; half 1
+                // keeps group k + 1 and receives the other half's group k + 1
+                const u32x2_t give = g ? mine[0] : mine[1];
+                const u32x2_t got = {partner(give[0]), partner(give[1])};
+                const u32x2_t lo = g ? got : mine[0], hi = g ? mine[1] : got;
+                if (q < N) {
+                    uint16_t *dst = static_cast<uint16_t *>(a.o) + head + (size_t)q * D + b * 32 + 8 * (k + g);
+                    *reinterpret_cast<u32x4_t *>(dst) = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
+        if (q < N && g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
     }
 };
 
