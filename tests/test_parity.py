@@ -185,6 +185,34 @@ def test_guard_bands_untouched():
     check(errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "bf16", "guard")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sixteen_byte_aligned_buffers(dtype):
+    """Inputs and outputs that start 16 bytes (the minimum the ABI accepts) past a
+    cache-line boundary, so every row and every 16-byte output store straddles lines."""
+    B, H, N, d = 1, 3, 277, 128
+    q, k, v = random_qkv(B, H, N, d, dtype, seed=11)
+    tdt = q.dtype
+    shift = 16 // q.element_size()
+    n = B * H * N * d
+    def place(t):
+        buf = torch.zeros(n + 64, dtype=tdt, device=DEV)
+        view = buf[shift:shift + n].view(B, H, N, d)
+        view.copy_(t)
+        return view
+    qd, kd, vd = place(q), place(k), place(v)
+    obuf = torch.zeros(n + 64, dtype=tdt, device=DEV)
+    o = obuf[shift:shift + n].view(B, H, N, d)
+    lbuf = torch.zeros(B * H * N + 16, dtype=torch.float32, device=DEV)
+    lse = lbuf[4:4 + B * H * N].view(B, H, N)
+    assert o.data_ptr() % 256 == 16 and qd.data_ptr() % 256 == 16
+    say(f"[align] {dtype} buffers at +16 bytes")
+    ea.attn_fwd(qd, kd, vd, causal=True, scale=0.09, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (obuf[:shift] == 0).all() and (obuf[shift + n:] == 0).all()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, 0.09, True)
+    check(errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), dtype, "aligned +16")
+
+
 def test_side_stream():
     q, k, v = (t.to(DEV) for t in random_qkv(1, 4, 257, 128, "f16", seed=3))
     s = torch.cuda.Stream()
