@@ -9,7 +9,9 @@ literal definition of scaled-dot-product attention with a causal lower-
 triangle mask, softmax over keys and the per-row log-sum-exp, following
 "Understand FlashAttention" (nothiny.github.io), sections "前向传播" and
 "附：数值稳定的logsumexp(L)推导", and "PyTorch profiling part 3: attention",
-section "朴素注意力" (naive attention).  This module only marshals arrays.
+section "朴素注意力" (naive attention); and its backward (dQ, dK, dV of a loss
+with gradient dO) from "Understand FlashAttention", section "反向传播".  This
+module only marshals arrays.
 
 Pins (tests/test_oracle.py) tie it to facts the pages and the mathematics fix;
 every function here is pinned (none is "parity unpinned").
@@ -61,6 +63,9 @@ class OracleLib:
         lib.oracle_attn_dense_f64.argtypes = [dp, dp, i64, i64, ctypes.c_double,
                                               ctypes.c_int, dp, dp]
         lib.oracle_attn_dense_f64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                            ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_bwd_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -113,6 +118,20 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_dense_f64 failed with status {rc}")
         return S, P
 
+    def attn_bwd(self, q, k, v, dout, scale: float, causal: bool):
+        """dQ, dK, dV of a loss whose gradient with respect to O is dout, all [B, H, N, d]
+        ("Understand FlashAttention", section "反向传播", with the scale on dQ and dK)."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        if q.ndim != 4 or any(t.shape != q.shape for t in (k, v, dout)):
+            raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+        B, H, N, d = q.shape
+        dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        rc = self.lib.oracle_attn_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), B, H, N, d, float(scale), int(bool(causal)))
+        if rc:
+            raise RuntimeError(f"oracle_attn_bwd_f64 failed with status {rc}")
+        return dq, dk, dv
+
 
 def _f64(x) -> np.ndarray:
     """Exact widening of a torch tensor or array to a C-contiguous fp64 array."""
@@ -149,3 +168,7 @@ def attn_rows(q, k, v, scale: float, causal: bool, rows):
 
 def attn_dense(q, k, scale: float, causal: bool):
     return default().attn_dense(q, k, scale, causal)
+
+
+def attn_bwd(q, k, v, dout, scale: float, causal: bool):
+    return default().attn_bwd(q, k, v, dout, scale, causal)

@@ -1,5 +1,5 @@
 /*
- * Reference attention forward in fp64 — TEST INFRASTRUCTURE ONLY.
+ * Reference attention forward and backward in fp64 — TEST INFRASTRUCTURE ONLY.
  *
  * This file is the oracle that the GPU path is checked against.  Only the
  * test suite, the smoke check and the CPU-baseline leg of the benchmark may
@@ -32,6 +32,9 @@
  *     o = 0 and lse = -inf, the "safe softmax" reading of that page's section
  *     "安全 softmax".  The library's boundary (equal query and key lengths,
  *     diagonal kept) never produces such a row.
+ *
+ * The backward (oracle_attn_bwd_f64, below) follows the same page's section
+ * "反向传播" and recomputes each softmax row from the definition.
  *
  * Every row materialises its whole score row s[0..N) in fp64; inputs are the
  * exact values the GPU sees, widened to double by the caller.  Summation is a
@@ -212,6 +215,96 @@ int oracle_attn_dense_f64(const double *q, const double *k, int64_t N,
         for (int64_t j = 0; j < N; ++j) p[j] /= l;
     }
     return 0;
+}
+
+/* Backward of the same attention, all heads (gradients of a scalar loss L
+ * whose gradient with respect to O is dout):
+ *
+ *   "Understand FlashAttention", section "Attention 前向和反向传播公式 /
+ *   反向传播": dV = P^T dO, dP = dO V^T, dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik),
+ *   dQ = dS K, dK = dS^T Q.  Here S = scale * Q K^T, so the chain rule puts
+ *   the scale on dQ and dK: dQ = scale * dS K, dK = scale * dS^T Q.  Masked
+ *   entries have P_ij = 0 and so contribute nothing.
+ *
+ * Each query row i is taken in turn: its softmax row P_i (recomputed from the
+ * definition, as in the forward), dP_i, the row term D_i = sum_j P_ij dP_ij,
+ * dS_i, then dQ_i, and its contributions to every dK_j and dV_j.  Heads are
+ * independent and are spread over OpenMP threads; inside a head the rows
+ * accumulate into dK and dV in order, so results are deterministic.
+ *   q, k, v, dout : [B, H, N, d] row-major fp64
+ *   dq, dk, dv    : [B, H, N, d] (written)
+ */
+int oracle_attn_bwd_f64(const double *q, const double *k, const double *v,
+                        const double *dout, double *dq, double *dk, double *dv,
+                        int64_t B, int64_t H, int64_t N, int64_t d,
+                        double scale, int causal)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    const int64_t heads = B * H;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *P = (double *)malloc((size_t)N * sizeof(double));
+        double *dP = (double *)malloc((size_t)N * sizeof(double));
+        if (!P || !dP) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t hd = 0; hd < heads; ++hd) {
+            if (!P || !dP) continue;
+            const int64_t base = hd * N * d;
+            const double *qh = q + base, *kh = k + base, *vh = v + base, *doh = dout + base;
+            double *dqh = dq + base, *dkh = dk + base, *dvh = dv + base;
+            for (int64_t t = 0; t < N * d; ++t) {
+                dkh[t] = 0.0;
+                dvh[t] = 0.0;
+            }
+            for (int64_t i = 0; i < N; ++i) {
+                const double *q_i = qh + i * d, *do_i = doh + i * d;
+                const int64_t nvis = causal ? i + 1 : N;  /* keys 0 .. nvis-1 are visible */
+                /* the softmax row, as in the forward */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += q_i[c] * kh[j * d + c];
+                    P[j] = dot * scale;
+                    if (P[j] > m) m = P[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    P[j] = exp(P[j] - m);
+                    l += P[j];
+                }
+                for (int64_t j = 0; j < nvis; ++j) P[j] /= l;
+                /* dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij */
+                double D = 0.0;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += do_i[c] * vh[j * d + c];
+                    dP[j] = dot;
+                    D += P[j] * dot;
+                }
+                /* dS_ij = P_ij (dP_ij - D_i); dQ_i = scale sum_j dS_ij k_j;
+                 * dK_j += scale dS_ij q_i; dV_j += P_ij dO_i */
+                double *dq_i = dqh + i * d;
+                for (int64_t c = 0; c < d; ++c) dq_i[c] = 0.0;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    const double ds = P[j] * (dP[j] - D);
+                    for (int64_t c = 0; c < d; ++c) {
+                        dq_i[c] += scale * ds * kh[j * d + c];
+                        dkh[j * d + c] += scale * ds * q_i[c];
+                        dvh[j * d + c] += P[j] * do_i[c];
+                    }
+                }
+            }
+        }
+        free(P);
+        free(dP);
+    }
+    return failed ? 2 : 0;
 }
 
 /* Number of OpenMP threads a parallel region of this library will use. */

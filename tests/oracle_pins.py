@@ -18,6 +18,8 @@ Sources (pages cited by title and section):
         - "缩放点积注意力" / "那么 math 后端有什么用？": torch's SDPA math path is a
           plain decomposition of the same operation (used as an independent library)
         - "构建因果掩码": the causal mask is the lower triangle (tril), key j <= query i
+  [FA]  "反向传播": dV = P^T dO, dP = dO V^T, dS = P o (dP - rowsum(P o dP)),
+        dQ = dS K, dK = dS^T Q (the backward pins below; S carries the scale)
 """
 from __future__ import annotations
 
@@ -331,6 +333,113 @@ def pin_heads_independent(orc):
             for h in range(H):
                 oh, lh = _one_head(orc, q[b, h], k[b, h], v[b, h], 0.5, causal)
                 assert np.array_equal(o[b, h], oh) and np.array_equal(lse[b, h], lh)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(orc, q, k, v, g, scale, causal):
+    """L = sum(O * g): its gradient with respect to O is g."""
+    o, _ = orc.attn_fwd(q, k, v, scale, causal)
+    return float(np.sum(o * g))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every entry of dQ, dK, dV equals the central difference of L = sum(O g) computed
+    with the forward oracle (a derivative fixed by the forward alone)."""
+    rng = np.random.default_rng(23)
+    B, H, N, d = 1, 2, 5, 3
+    h = 1e-5
+    for causal in (False, True):
+        q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+        grads = orc.attn_bwd(q, k, v, g, 0.8, causal)
+        for which, grad in enumerate(grads):
+            num = np.empty_like(grad)
+            for idx in np.ndindex(grad.shape):
+                args = [q, k, v]
+                plus = [a.copy() for a in args]
+                minus = [a.copy() for a in args]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                num[idx] = (_loss(orc, *plus, g, 0.8, causal) - _loss(orc, *minus, g, 0.8, causal)) / (2 * h)
+            _close(grad, num, 1e-8, f"finite differences {'qkv'[which]} causal={causal}")
+
+
+def pin_bwd_constant_values(orc):
+    """Equal V rows make O independent of the weights, so dQ = dK = 0; dV still
+    carries P^T dO ([FA] 反向传播: dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik) with dP_ij
+    the same for every j)."""
+    rng = np.random.default_rng(24)
+    B, H, N, d = 1, 2, 11, 6
+    q, k, g = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    v = np.broadcast_to(rng.standard_normal(d), (B, H, N, d)).copy()
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd(q, k, v, g, 0.6, causal)
+        _close(dq, np.zeros_like(dq), 1e-13, "constant V: dQ")
+        _close(dk, np.zeros_like(dk), 1e-13, "constant V: dK")
+        assert np.max(np.abs(dv)) > 1e-2
+
+
+def pin_bwd_sums(orc):
+    """Rows of P sum to 1, so sum_j dV_j = sum_i dO_i; rows of dS sum to 0, so
+    sum_j dK_j = 0 (both hold causal or not)."""
+    rng = np.random.default_rng(25)
+    B, H, N, d = 2, 2, 13, 5
+    for causal in (False, True):
+        q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+        dq, dk, dv = orc.attn_bwd(q, k, v, g, 0.45, causal)
+        _close(dv.sum(axis=2), g.sum(axis=2), 1e-12, "sum of dV rows")
+        _close(dk.sum(axis=2), np.zeros((B, H, d)), 1e-12, "sum of dK rows")
+
+
+def pin_bwd_closed_forms(orc):
+    """Causal row 0 sees key 0 only: P_00 = 1, dS_0. = 0, so dQ_0 = 0 exactly.  Scale 0:
+    dQ = dK = 0 exactly, and P is uniform over the allowed keys, so
+    dV_j = sum_{i >= j} dO_i / (i + 1) (causal) or mean_i dO_i (not causal)."""
+    rng = np.random.default_rng(26)
+    B, H, N, d = 1, 1, 9, 4
+    q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    dq, _, _ = orc.attn_bwd(q, k, v, g, 0.9, True)
+    assert np.all(dq[0, 0, 0] == 0.0)
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd(q, k, v, g, 0.0, causal)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        if causal:
+            w = np.array([[1.0 / (i + 1) if j <= i else 0.0 for j in range(N)] for i in range(N)])
+        else:
+            w = np.full((N, N), 1.0 / N)
+        _close(dv[0, 0], w.T @ g[0, 0], 1e-14, f"scale 0 dV causal={causal}")
+
+
+def pin_bwd_torch_autograd(orc):
+    """Cross-check with torch autograd through its CPU fp64 SDPA math path, an
+    independent implementation of the same derivative ([PT] math backend)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(27)
+    for (B, H, N, d) in [(1, 1, 1, 1), (2, 3, 7, 16), (1, 2, 40, 64)]:
+        for causal in (False, True):
+            q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+            scale = 1.0 / math.sqrt(d)
+            dq, dk, dv = orc.attn_bwd(q, k, v, g, scale, causal)
+            tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+            out = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+            out.backward(torch.from_numpy(g))
+            for mine, ref, name in ((dq, tq.grad, "dQ"), (dk, tk.grad, "dK"), (dv, tv.grad, "dV")):
+                _close(mine, ref.numpy(), 1e-12, f"autograd {name} {B,H,N,d,causal}")
+
+
+def pin_bwd_heads_independent(orc):
+    """A batched backward equals per-head backward calls."""
+    rng = np.random.default_rng(28)
+    B, H, N, d = 2, 2, 8, 3
+    q, k, v, g = rng.standard_normal((4, B, H, N, d))
+    dq, dk, dv = orc.attn_bwd(q, k, v, g, 0.5, True)
+    for b in range(B):
+        for hh in range(H):
+            one = orc.attn_bwd(q[b:b + 1, hh:hh + 1], k[b:b + 1, hh:hh + 1], v[b:b + 1, hh:hh + 1],
+                               g[b:b + 1, hh:hh + 1], 0.5, True)
+            for full, part in zip((dq, dk, dv), one):
+                assert np.array_equal(full[b, hh], part[0, 0])
 
 
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

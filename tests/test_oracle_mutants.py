@@ -38,6 +38,19 @@ MUTANTS = [
     ("rows_head_offset", "attention_row(q + i * d, k, v, N, d, scale, causal, i, s,",
      "attention_row(q + i * d, k, v, N, d, scale, causal, 0, s,"),
     ("batched_head_offset", "const int64_t base = head * N * d;", "const int64_t base = (head / 2) * N * d;"),
+    # backward
+    ("bwd_dk_scale_dropped", "dkh[j * d + c] += scale * ds * q_i[c];", "dkh[j * d + c] += ds * q_i[c];"),
+    ("bwd_dq_scale_dropped", "dq_i[c] += scale * ds * kh[j * d + c];", "dq_i[c] += ds * kh[j * d + c];"),
+    ("bwd_row_term_dropped", "const double ds = P[j] * (dP[j] - D);", "const double ds = P[j] * dP[j];"),
+    ("bwd_row_term_unweighted", "D += P[j] * dot;", "D += dot;"),
+    ("bwd_dk_uses_key", "dkh[j * d + c] += scale * ds * q_i[c];", "dkh[j * d + c] += scale * ds * kh[j * d + c];"),
+    ("bwd_dv_uses_ds", "dvh[j * d + c] += P[j] * do_i[c];", "dvh[j * d + c] += ds * do_i[c];"),
+    ("bwd_dp_uses_key", "for (int64_t c = 0; c < d; ++c) dot += do_i[c] * vh[j * d + c];",
+     "for (int64_t c = 0; c < d; ++c) dot += do_i[c] * kh[j * d + c];"),
+    ("bwd_mask_drops_diagonal", "const int64_t nvis = causal ? i + 1 : N;", "const int64_t nvis = causal ? i : N;"),
+    ("bwd_not_normalised", "for (int64_t j = 0; j < nvis; ++j) P[j] /= l;", "for (int64_t j = 0; j < nvis; ++j) P[j] /= (l + 0.5);"),
+    ("bwd_scores_unscaled", "P[j] = dot * scale;\n                    if (P[j] > m) m = P[j];",
+     "P[j] = dot;\n                    if (P[j] > m) m = P[j];"),
 ]
 
 
