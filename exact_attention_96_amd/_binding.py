@@ -1,8 +1,9 @@
 """ctypes binding of libattn.so (argument marshalling only).
 
-Every step of the forward runs in the HIP library; this module checks the
-tensors, allocates the outputs with torch and passes raw device pointers and
-torch's current HIP stream to ``attn_fwd`` (declared in include/attn.h).
+Every step of the forward and backward runs in the HIP library; this module
+checks the tensors, allocates the outputs with torch and passes raw device
+pointers and torch's current HIP stream to ``attn_fwd`` and ``attn_bwd``
+(declared in include/attn.h).
 There is no fallback: a missing library or a failed call raises.
 """
 from __future__ import annotations
@@ -21,8 +22,8 @@ _lib = None
 
 
 class AttnError(RuntimeError):
-    def __init__(self, status: int, msg: str):
-        super().__init__(f"attn_fwd failed: status {status} ({msg})")
+    def __init__(self, status: int, msg: str, call: str = "attn_fwd"):
+        super().__init__(f"{call} failed: status {status} ({msg})")
         self.status = status
 
 
@@ -39,6 +40,9 @@ def lib() -> ctypes.CDLL:
         ci = ctypes.c_int
         L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
         L.attn_fwd.restype = ci
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float,
+                               ci, ci, vp]
+        L.attn_bwd.restype = ci
         L.attn_strerror.argtypes = [ci]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
@@ -60,6 +64,14 @@ def attn_fwd_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: in
     """Raw call with integer device addresses; returns the status code."""
     return int(lib().attn_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
                               causal, dtype, stream))
+
+
+def attn_bwd_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+                 delta: int, B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+                 stream: int) -> int:
+    """Raw call with integer device addresses; returns the status code."""
+    return int(lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d,
+                              ctypes.c_float(scale), causal, dtype, stream))
 
 
 def _dtype_code(t) -> int:
@@ -113,3 +125,64 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     if st != ATTN_OK:
         raise AttnError(st, strerror(st))
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, delta=None):
+    """Attention backward on the GPU.
+
+    q, k, v, o, dout: torch tensors [B, H, N, d] on one HIP device, one dtype
+    (float16 or bfloat16), contiguous; o and lse (float32 [B, H, N]) are the
+    forward's outputs for the same q, k, v, causal and scale.  Returns
+    (dq, dk, dv), each like q.  ``delta`` is an optional float32 [B, H, N]
+    workspace (written with dO_i . O_i).  ``scale`` defaults to 1/sqrt(d) rounded
+    to fp32.  The call is enqueued on torch's current stream.
+    """
+    import torch
+    ts = {"q": q, "k": k, "v": v, "o": o, "dout": dout}
+    for name, t in ts.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4 or t.shape != q.shape:
+            raise ValueError(f"{name} must have q's [B, H, N, d] shape {tuple(q.shape)}, got {tuple(t.shape)}")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o, dout must share one dtype")
+        if t.device != q.device:
+            raise ValueError("q, k, v, o, dout must be on one device")
+    code = _dtype_code(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def _vec(t, name):
+        if t is None:
+            return torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        if t.shape != (B, H, N) or t.dtype != torch.float32 or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, N] tensor on q's device")
+        return t
+
+    def _like(t, name):
+        if t is None:
+            return torch.empty_like(q)
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+        return t
+
+    if not isinstance(lse, torch.Tensor):
+        raise TypeError("lse must be a torch.Tensor")
+    lse = _vec(lse, "lse")
+    delta = _vec(delta, "delta")
+    dq, dk, dv = _like(dq, "dq"), _like(dk, "dk"), _like(dv, "dv")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          delta.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, strerror(st), "attn_bwd")
+    return dq, dk, dv

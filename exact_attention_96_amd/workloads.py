@@ -104,3 +104,12 @@ def random_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int, std: float
     """Q, K, V for an ad-hoc shape (parity sweeps), same recipe as make_inputs."""
     w = Workload("adhoc", B, H, N, d, dtype, False, std=std, seed=seed)
     return make_inputs(w)
+
+
+def random_grad(B: int, H: int, N: int, d: int, dtype: str, seed: int, std: float = 1.0):
+    """Upstream gradient dO (CPU tensor [B, H, N, d] in `dtype`): i.i.d. N(0, std^2),
+    the gradient of a random linear loss sum(O * G)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return (torch.randn((B, H, N, d), dtype=torch.float32, generator=g) * std).to(dt)

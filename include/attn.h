@@ -1,5 +1,6 @@
 /*
- * attn.h — C ABI of the exact attention forward library for MI355X (gfx950).
+ * attn.h — C ABI of the exact attention library for MI355X (gfx950):
+ * forward (attn_fwd) and backward (attn_bwd).
  *
  * The operation is exact scaled-dot-product attention, one (batch, head) at a
  * time:
@@ -94,6 +95,53 @@ typedef enum {
 ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                       int B, int H, int N, int d, float scale, int causal, int dtype,
                       hipStream_t stream);
+
+/*
+ * attn_bwd — gradients of attention for B*H independent heads.
+ *
+ * Given dO = dLoss/dO for the forward above, computes dQ, dK, dV following
+ * "Understand FlashAttention" (nothiny.github.io), section "反向传播":
+ *
+ *   dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij = dO_i . O_i,
+ *   dS = P o (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,
+ *
+ * with P recomputed tile by tile from the forward's lse (same page, section
+ * "为什么保存 logsumexp": P_ij = e^{S_ij - lse_i}), so nothing N x N reaches
+ * device memory.
+ *
+ * Arguments
+ *   q, k, v  as in attn_fwd; read only.
+ *   o, lse   the forward's outputs for these q, k, v, scale and causal; read only.
+ *   dout     device pointer, [B, H, N, d] contiguous of `dtype`; read only.
+ *   dq, dk, dv  device pointers, [B, H, N, d] contiguous of `dtype`; written,
+ *            rounded to `dtype` (nearest even).
+ *   delta    device pointer, [B, H, N] contiguous fp32 workspace owned by the
+ *            caller; written with D_i = dO_i . O_i (fp32).
+ *   B, H, N, d, scale, causal, stream  as in attn_fwd.
+ *   dtype    ATTN_BF16 or ATTN_F16 (ATTN_F32 is ATTN_EUNSUPPORTED).
+ *
+ * Arithmetic: products on the matrix cores with fp32 accumulation; P and dS
+ * are rounded to the input type before the products that consume them.
+ * Results of one build on one input are bitwise reproducible (no atomics).
+ *
+ * Ownership and concurrency: as attn_fwd.  dq, dk, dv and delta must not
+ * overlap any input or each other.
+ *
+ * Errors are returned synchronously and nothing is launched on error:
+ *   ATTN_EINVAL       a NULL pointer; B, H or N < 1; d < 1; unknown dtype;
+ *                     causal not 0/1; non-finite scale; a [B, H, N, d] buffer
+ *                     not 16-byte aligned or lse/delta not 4-byte aligned; an
+ *                     output overlapping an input or another output.
+ *   ATTN_EUNSUPPORTED dtype ATTN_F32; d not 64 or 128; a problem whose tile
+ *                     count exceeds the launch grid.
+ *   ATTN_EHIP         a launch failed (its own status).  Launches before the
+ *                     failing one stay enqueued.
+ * The call is asynchronous: results are valid once `stream` has completed.
+ */
+ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                      float *delta, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 ATTN_API const char *attn_strerror(int status);

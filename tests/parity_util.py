@@ -45,3 +45,52 @@ def sample_rows(N: int, rng: np.random.Generator, n_random: int = 48) -> np.ndar
              N - 129, N - 128, N - 127, N - 65, N - 64, N - 33, N - 32, N - 2, N - 1]
     rows = [r for r in fixed if 0 <= r < N] + list(rng.integers(0, N, size=n_random))
     return np.unique(np.array(rows, dtype=np.int64))
+
+
+# Backward bars.  Every gradient element is a sum of products in which one factor
+# (P, or dS = P o (dP - D)) is rounded once to the input type before the matrix
+# core multiplies it, and the result is rounded once more on the store, so its
+# error is a few units of roundoff u of that type relative to the size of its row
+# (u = 2^-8 for bf16, 2^-11 for fp16).  The error of each element is therefore
+# measured against the RMS of its own row of the exact gradient (row sizes differ by
+# orders of magnitude under the causal mask), with a floor of 1% of the whole
+# tensor's RMS for rows whose exact gradient vanishes (dQ of the first causal
+# query is exactly zero):
+#   max over elements of |err| / (8 u base)  <= 1,   mean of |err| / base <= u,
+# base = row RMS + 1% of the tensor RMS.
+# dQ carries one more term.  D_i = dO_i . O_i is formed from the forward's output
+# O, which is rounded to the input type, so D_i is off by up to
+# u sum_c |dO_ic O_ic|; every dS_ij of the row moves by -P_ij times that, and dQ_i
+# by -scale (sum_j P_ij k_j) times it.  Where dP_ij - D_i cancels (a causal row
+# with two or three keys) this term is the larger one, so the dQ bar adds
+#   t_ic = scale u (sum_c' |dO_ic' O*_ic'|) |(P K)_ic|
+# to the allowance, with O* and P K taken from the oracle's forward.
+BWD_U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def bwd_errors(g_gpu, g_ref, u: float, extra=None) -> dict:
+    """Errors of one gradient tensor [..., N, d] against the exact one (see above)."""
+    g = np.asarray(g_gpu, dtype=np.float64)
+    r = np.asarray(g_ref, dtype=np.float64)
+    rms_all = float(np.sqrt(np.mean(r * r)))
+    base = np.sqrt(np.mean(r * r, axis=-1, keepdims=True)) + 1e-2 * rms_all + 1e-300
+    e = np.abs(g - r)
+    allow = 8 * u * base + (0.0 if extra is None else extra)
+    return dict(ratio=float((e / allow).max()), mean=float((e / base).mean()) / u,
+                max_u=float((e / base).max()) / u, finite=bool(np.isfinite(g).all()),
+                abs_max=float(e.max()), rms=rms_all)
+
+
+def bwd_check(err: dict, what: str) -> None:
+    assert err["finite"], f"{what}: non-finite gradient"
+    assert err["ratio"] <= 1.0, f"{what}: error {err['ratio']:.3f} x the allowance"
+    assert err["mean"] <= 1.0, f"{what}: mean row-relative error {err['mean']:.3f} u > 1 u"
+
+
+def dq_extra(q, k, v, dout, scale: float, causal: bool, u: float, oracle_mod):
+    """The dQ allowance t (above) from the oracle's forward of (Q, K, V) and of (Q, K, K)."""
+    o_ref, _ = oracle_mod.attn_fwd(q, k, v, scale, causal)
+    pk, _ = oracle_mod.attn_fwd(q, k, k, scale, causal)
+    dof = np.asarray(dout.double().numpy() if hasattr(dout, "double") else dout, dtype=np.float64)
+    dD = u * np.sum(np.abs(dof * o_ref), axis=-1, keepdims=True)
+    return scale * dD * np.abs(pk)

@@ -19,7 +19,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["attn_abi_version", "attn_fwd", "attn_strerror"]
+    assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -87,3 +87,41 @@ def test_lse_just_after_o_is_fine_to_check():
     # o occupies B*H*N*d*2 bytes; lse placed right after it does not overlap o.
     nbytes = 2 * 3 * 100 * 64 * 2
     assert call(dtype=7, lse=O + nbytes) == ea.ATTN_EINVAL  # rejected for the dtype only
+
+
+# attn_bwd: the same host checks, with its extra buffers.
+DO, DQ, DK, DV, DL = (i << 40 for i in range(6, 11))
+GOOD_BWD = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, H=3, N=100,
+                d=64, scale=0.125, causal=1, dtype=2, stream=0)
+BWD_ORDER = ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "H", "N", "d",
+             "scale", "causal", "dtype", "stream"]
+
+
+def call_bwd(**kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return ea.attn_bwd_ptr(*(a[n] for n in BWD_ORDER))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(o=0), dict(lse=0), dict(dout=0), dict(dq=0), dict(dk=0), dict(dv=0),
+    dict(delta=0), dict(B=0), dict(N=-1), dict(d=0), dict(dtype=5), dict(causal=3),
+    dict(scale=float("nan")), dict(dout=DO + 8), dict(dq=DQ + 4), dict(dv=DV + 2),
+    dict(delta=DL + 1), dict(lse=L + 2),
+    dict(dq=Q), dict(dk=O + 32), dict(dv=DO - 16), dict(delta=L), dict(delta=DQ + 64),
+    dict(dk=DQ + 16), dict(dv=DK), dict(dq=DL - 16),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_bwd_invalid_arguments(kw):
+    assert call_bwd(**kw) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(d=32), dict(d=96), dict(d=256),
+                                dict(B=65536, H=65536, N=1, d=64)])
+def test_bwd_unsupported(kw):
+    assert call_bwd(**kw) == ea.ATTN_EUNSUPPORTED
+
+
+def test_bwd_outputs_right_after_inputs_are_fine():
+    # dq placed right after dout (tensor bytes 2*3*100*64*2) does not overlap it.
+    nbytes = 2 * 3 * 100 * 64 * 2
+    assert call_bwd(dq=DO + nbytes, dtype=9) == ea.ATTN_EINVAL  # rejected for the dtype only
