@@ -1,6 +1,6 @@
-"""Throughput of the fused attention forward on one MI355X.
+"""Throughput of the fused attention forward (or backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3] [--pass fwd|bwd]
 
 A step is one call of attn_fwd (the whole fused forward: Q tile load, K/V
 staging, both matrix products, online softmax, normalisation, O and lse
@@ -9,6 +9,10 @@ The default workload is causal bf16 attention with B=2, H=32, N=8192, d=128.
 Prints one JSON line: throughput in TFLOP/s at the algorithmic count
 4*B*H*N^2*d (halved when causal), the kernel's roofline figures, and the fp64
 CPU oracle timed on a bounded sample of the same workload on the host cores.
+
+With --pass bwd a step is one call of attn_bwd (D = rowsum(dO o O), then the
+dQ and dK/dV kernels) on the forward's o and lse, counted at 2.5 times the
+forward's flops (five N x N x d products instead of two).
 """
 from __future__ import annotations
 
@@ -124,6 +128,29 @@ def cpu_baseline(w, q, k, v, seconds: float):
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
 
+def cpu_baseline_bwd(w, q, k, v, do, seconds: float):
+    """The fp64 oracle backward on whole heads of the same workload, as many at once as
+    the oracle has threads (it runs heads in parallel), batch after batch until
+    `seconds` of wall time have been spent (at least one batch)."""
+    import oracle
+    T = max(1, oracle.num_threads())
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(heads):
+        batch = heads[done:done + T]
+        sel = lambda x: x[[b for b, _ in batch], [h for _, h in batch]][None]  # noqa: E731
+        oracle.attn_bwd(sel(q), sel(k), sel(v), sel(do), w.scale, w.causal)
+        done += len(batch)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops * done / (w.B * w.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": T, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads, whole heads, {min(T, done)} at a time "
+                      f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
+
+
 def copy_probe(nbytes: int, steps: int):
     """A plain device copy of known size (counter calibration run)."""
     import torch
@@ -142,6 +169,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", help="c1..c5 (default: c3, the headline)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle runs whole heads for cpu_baseline (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=None, help="(0: skip the cpu_baseline leg)")
@@ -169,7 +198,7 @@ def main():
 
     import torch
     import exact_attention_96_amd as ea
-    from exact_attention_96_amd.workloads import WORKLOADS, make_inputs
+    from exact_attention_96_amd.workloads import WORKLOADS, make_inputs, random_grad
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
@@ -183,8 +212,23 @@ def main():
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
-    def step():
+    bwd = args.which == "bwd"
+    if bwd:
+        if w.dtype == "f32":
+            print("the backward runs in bf16/fp16 only", file=sys.stderr)
+            sys.exit(2)
+        do = random_grad(w.B, w.H, w.N, w.d, w.dtype, w.seed + 1000, std=w.std)
+        dod = do.to(dev)
         ea.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+        delta = torch.empty_like(lse)
+
+        def step():
+            ea.attn_bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                        delta=delta)
+    else:
+        def step():
+            ea.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -206,13 +250,15 @@ def main():
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
-    value = w.flops * args.steps / wall / 1e12
+    flops = 2.5 * w.flops if bwd else w.flops
+    value = flops * args.steps / wall / 1e12
 
-    achieved = w.flops / avg_kernel_s / 1e12
+    achieved = flops / avg_kernel_s / 1e12
     peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_MFMA_BF16_TFLOPS
-    traffic = measured_traffic(w.name)
+    traffic = None if bwd else measured_traffic(w.name)
     out = {
-        "metric": "attention fwd TFLOP/s (bf16 causal, N=8192 d=128) and % of MFMA peak",
+        "metric": ("attention bwd TFLOP/s (bf16 causal, N=8192 d=128) and % of MFMA peak" if bwd else
+                   "attention fwd TFLOP/s (bf16 causal, N=8192 d=128) and % of MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_of_mfma_peak": round(100 * value / peak, 2),
@@ -229,13 +275,17 @@ def main():
                    "causal": w.causal, "scale": w.scale},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "algorithmic_bytes": w.io_bytes,
+                     "traffic": traffic,
+                     # backward: q, k, v, o, dO and lse read, dq, dk, dv written, once each
+                     "algorithmic_bytes": (8 * w.B * w.H * w.N * w.d * w.elt + 4 * w.B * w.H * w.N
+                                           if bwd else w.io_bytes),
                      "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
                      "kernel_source_sha": kernel_source_hash()},
     }
     if args.cpu_seconds > 0 and args.cpu_heads != 0:
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds) if bwd else
+                               cpu_baseline(w, q, k, v, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

@@ -22,8 +22,9 @@
 // from the vector ALU to the matrix core without leaving registers.  The
 // transposed operands (K^T, dO^T, Q^T) come from the same row-major LDS blocks
 // through ds_read_b64_tr_b16.  LDS rows carry their 16-byte chunks at
-// chunk ^ swz(row), a swizzle that depends only on bits of the row that the
-// transposing reads keep fixed.
+// chunk ^ swz(row), a swizzle under which both kinds of read are free of bank
+// conflicts: sixteen consecutive rows read at one chunk land on sixteen different
+// bank groups, and so do the four rows by four chunks of one transposing read.
 #pragma once
 
 #include "fwd_mfma.hpp"
@@ -85,9 +86,13 @@ struct BwdCommon {
     typedef Mfma<T> M;
     typedef typename M::v8 v8;
     static __device__ __forceinline__ v8 as_v8(u32x4_t x) { return __builtin_bit_cast(v8, x); }
-    // chunk swizzle: a function of row bits 0-1 (d = 128) or bit 1 (d = 64) only, so the
-    // transposing reads (rows r, r + 4, r + 16) see one swizzle per lane
-    static __device__ __forceinline__ int swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+    // chunk swizzle.  d = 128 (a row spans all 64 banks): rows 0..15 get 16 different
+    // values, and rows 4m .. 4m + 3 different multiples of 4 (different 64-byte quads).
+    // d = 64 (two rows per 256 bytes): the same for the even and for the odd rows.
+    // Depends on bits 0-3 of the row only, so rows r and r + 16 share it.
+    static __device__ __forceinline__ int swz(int r) {
+        return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    }
 
     // A operand from the rows of a block: lane reads row sigma(l32), k-step cc.
     static __device__ __forceinline__ v8 row_frag(uint32_t base, int l32, int g, int cc) {
@@ -101,11 +106,13 @@ struct BwdCommon {
     // A operand X^T (32 columns of d in block db, 16 rows kc of the block) by transposing reads.
     static __device__ __forceinline__ v8 tr_frag(uint32_t base, int lane, int db, int kc) {
         const int j16 = lane & 15, grp = lane >> 4;
-        const int r = 8 * (grp >> 1) + (j16 >> 2) + 16 * kc;
+        const int r = 8 * (grp >> 1) + (j16 >> 2);  // and r + 4; both plus 16 kc
         const int cl = 2 * (grp & 1) + ((j16 & 3) >> 1);
-        const uint32_t a = base + r * ROWB + (((4 * db + cl) ^ swz(r)) << 4) + 8 * (j16 & 1);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(a));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(a + 4 * ROWB));
+        const uint32_t a = base + 16 * kc * ROWB + 8 * (j16 & 1);
+        const uint32_t alo = a + r * ROWB + (((4 * db + cl) ^ swz(r)) << 4);
+        const uint32_t ahi = a + (r + 4) * ROWB + (((4 * db + cl) ^ swz(r + 4)) << 4);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(alo));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(ahi));
         const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
         return as_v8((u32x4_t){l2[0], l2[1], h2[0], h2[1]});
     }
@@ -287,16 +294,42 @@ struct BwdDkv : BwdCommon<T, D> {
     using C::DC;
     typedef typename C::M M;
     typedef typename C::v8 v8;
-    static constexpr int NW = 4, THREADS = NW * 64;
-    static constexpr int BKV = NW * 32;              // key rows per workgroup
+    // Two groups of four waves share the workgroup's 128 keys (wave w & 3 of either
+    // group owns keys 32 (w & 3) ..) and take alternate query blocks, so that each SIMD
+    // runs two waves; their partial dK and dV are added through LDS at the end.
+    static constexpr int NW = 8, GW = 4, THREADS = NW * 64;
+    static constexpr int BKV = GW * 32;              // key rows per workgroup
     static constexpr int BQ = 32;                    // queries per streamed block
     static constexpr int KV_B = 2 * BKV * ROWB;      // resident K then V tile
     static constexpr int BLK_B = BQ * ROWB;          // one Q or dO block
     static constexpr int STAGE_B = 2 * BLK_B + 256;  // Q, dO, then L (32 floats) and D (32 floats)
-    static constexpr int LDS_B = KV_B + 2 * STAGE_B;
-    static constexpr int LOADS = 2 * BLK_B / 1024 / NW;  // Q/dO loads per wave and block
+    static constexpr int RING_B = 2 * STAGE_B;       // two stages per group
+    static constexpr int LDS_B = KV_B + 2 * RING_B;
+    static constexpr int LOADS = 2 * BLK_B / 1024 / GW;  // Q/dO loads per wave and block
     static constexpr int KV_LOADS = KV_B / 1024 / NW;
-    static_assert(LOADS * 1024 * NW == 2 * BLK_B && KV_LOADS * 1024 * NW == KV_B, "loads split evenly");
+    static constexpr int PART_B = GW * DB * 16 * 64 * 4;  // one group's dK (or dV) partials, fp32
+    static_assert(LOADS * 1024 * GW == 2 * BLK_B && KV_LOADS * 1024 * NW == KV_B, "loads split evenly");
+    static_assert(PART_B <= KV_B && PART_B <= 2 * RING_B, "partials fit in the freed LDS");
+
+    static __device__ __forceinline__ void put_part(const f32x16_t (&acc)[DB], uint32_t base, int lane) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                *(lds_u32x4_t *)(uintptr_t)(base + (b * 4 + t) * 1024 + lane * 16) =
+                    (u32x4_t){__float_as_uint(acc[b][4 * t]), __float_as_uint(acc[b][4 * t + 1]),
+                              __float_as_uint(acc[b][4 * t + 2]), __float_as_uint(acc[b][4 * t + 3])};
+    }
+    static __device__ __forceinline__ void add_part(f32x16_t (&acc)[DB], uint32_t base, int lane) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4_t x = *(const lds_u32x4_t *)(uintptr_t)(base + (b * 4 + t) * 1024 + lane * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[b][4 * t + e] += __uint_as_float(x[e]);
+            }
+    }
 
     static __device__ void run(const BwdArgs &a) {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -320,11 +353,12 @@ struct BwdDkv : BwdCommon<T, D> {
         const float *del_h = a.delta + (size_t)bh * N;
         const int tid = threadIdx.x;
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int grp = w / GW, wk = w % GW;    // group, wave within the group
         const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
         const int kv0 = kt * BKV;               // first key of the workgroup
-        const int k0 = kv0 + 32 * w, key = k0 + l32;
+        const int k0 = kv0 + 32 * wk, key = k0 + l32;
         const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
-        const uint32_t kres = lds0, vres = lds0 + BKV * ROWB, st0 = lds0 + KV_B;
+        const uint32_t kres = lds0, vres = lds0 + BKV * ROWB, ring = lds0 + KV_B + grp * RING_B;
 
         f32x16_t dk[DB], dv[DB];
 #pragma unroll
@@ -343,42 +377,44 @@ struct BwdDkv : BwdCommon<T, D> {
                 C::load_rows(isv ? Vh : Kh, kv0, N, isv ? vres : kres, ch % PER, 1, lane);
             }
         }
-        const int nqb_all = (N + BQ - 1) / BQ;
+        const int nqb = (N + BQ - 1) / BQ;
         const int qb0 = CAUSAL ? kv0 / BQ : 0;      // queries before kv0 see none of these keys
         const int my_first = CAUSAL ? k0 / BQ : 0;  // first block with a query >= this wave's first key
+        const int iters = (nqb - qb0 + 1) / 2;      // group grp takes blocks qb0 + 2 it + grp
         const bool active = k0 < N;
-        auto issue = [&](int i) {
-            const uint32_t st = st0 + ((i - qb0) & 1) * STAGE_B;
+        auto issue = [&](int i, int it) {
+            const uint32_t st = ring + (it & 1) * STAGE_B;
             constexpr int PER = BLK_B / 1024;
 #pragma unroll
             for (int t = 0; t < LOADS; ++t) {
-                const int ch = w * LOADS + t;
+                const int ch = wk * LOADS + t;
                 const bool isd = ch >= PER;
                 C::load_rows(isd ? dOh : Qh, i * BQ, N, st + (isd ? BLK_B : 0), ch % PER, 1, lane);
             }
-            // L of the block's 32 queries (lanes 0-31) and D (lanes 32-63); every wave issues
-            // the same load (identical bytes), so that all waves count the same loads
+            // L of the block's 32 queries (lanes 0-31) and D (lanes 32-63); every wave of
+            // the group issues the same load (identical bytes), so all count the same loads
             const int qi = min(i * BQ + l32, N - 1);
             dma_to_lds4(g ? (const void *)(del_h + qi) : (const void *)(lse_h + qi), st + 2 * BLK_B);
         };
 
-        if (qb0 < nqb_all) issue(qb0);
-        for (int i = qb0; i < nqb_all; ++i) {
-            if (i + 1 < nqb_all) {
-                issue(i + 1);
+        if (qb0 + grp < nqb) issue(qb0 + grp, 0);
+        for (int it = 0; it < iters; ++it) {
+            const int i = qb0 + 2 * it + grp;
+            if (i + 2 < nqb) {
+                issue(i + 2, it + 1);
                 bwd_barrier<LOADS + 1>();
             } else {
                 bwd_barrier<0>();
             }
-            if (active && i >= my_first) {
-                const uint32_t qb = st0 + ((i - qb0) & 1) * STAGE_B, ob = qb + BLK_B, lb = qb + 2 * BLK_B;
+            if (active && i < nqb && i >= my_first) {
+                const uint32_t qb = ring + (it & 1) * STAGE_B, ob = qb + BLK_B, lb = qb + 2 * BLK_B;
                 f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    s = M::mma(C::row_frag(qb, l32, g, cc), C::col_frag(kres, 32 * w + l32, g, cc), s);
+                    s = M::mma(C::row_frag(qb, l32, g, cc), C::col_frag(kres, 32 * wk + l32, g, cc), s);
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    dp = M::mma(C::row_frag(ob, l32, g, cc), C::col_frag(vres, 32 * w + l32, g, cc), dp);
+                    dp = M::mma(C::row_frag(ob, l32, g, cc), C::col_frag(vres, 32 * wk + l32, g, cc), dp);
                 // register i of half g holds query i BQ + 16 (i >> 3) + 8 g + (i & 7); lane = key
                 uint32_t pp[2][4], pd[2][4];
 #pragma unroll
@@ -422,12 +458,25 @@ struct BwdDkv : BwdCommon<T, D> {
             bwd_barrier<0>();
         }
         // a workgroup with no query block still waits for its resident loads
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        bwd_barrier<0>();
+        // group 1 hands its dK partials to group 0 (in the freed rings), group 0 its dV
+        // partials to group 1 (in the freed K/V tile); each then finishes one output
+        const uint32_t part_k = lds0 + KV_B + wk * (PART_B / GW), part_v = lds0 + wk * (PART_B / GW);
+        if (grp == 1)
+            put_part(dk, part_k, lane);
+        else
+            put_part(dv, part_v, lane);
+        bwd_barrier<0>();
         const int kc_ = min(key, N - 1);
-        uint16_t *dkp = static_cast<uint16_t *>(a.dk) + head + (size_t)kc_ * D;
-        uint16_t *dvp = static_cast<uint16_t *>(a.dv) + head + (size_t)kc_ * D;
-        C::store_rows(dk, a.scale, dkp, key < N, g);
-        C::store_rows(dv, 1.f, dvp, key < N, g);
+        if (grp == 0) {
+            add_part(dk, part_k, lane);
+            uint16_t *dkp = static_cast<uint16_t *>(a.dk) + head + (size_t)kc_ * D;
+            C::store_rows(dk, a.scale, dkp, key < N, g);
+        } else {
+            add_part(dv, part_v, lane);
+            uint16_t *dvp = static_cast<uint16_t *>(a.dv) + head + (size_t)kc_ * D;
+            C::store_rows(dv, 1.f, dvp, key < N, g);
+        }
     }
 };
 
@@ -437,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     BwdDkv<T, D, CAUSAL>::run(a);
 }
 
