@@ -258,17 +258,25 @@ struct BwdDq : BwdCommon<T, D> {
                 for (int cc = 0; cc < DC; ++cc) s = M::mma(C::row_frag(kb, l32, g, cc), qT[cc], s);
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc) dp = M::mma(C::row_frag(vb, l32, g, cc), doT[cc], dp);
+                // fragment reads run three ahead of the products that use them
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3, 0);
+                sched_mfma_reads<2 * DC, 1, 2 * DC - 3>();
                 // register i of half g holds key j BK + 16 (i >> 3) + 8 g + (i & 7)
-                const int lim = last_key - j * BK - 8 * g;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], a.c, nlse));
+                // only blocks not wholly visible to every query of the wave are masked
+                if ((CAUSAL && j * BK + BK - 1 > q0) || j * BK + BK > N) {
+                    const int lim = last_key - j * BK - 8 * g;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[i] = 16 * (i >> 3) + (i & 7) <= lim ? s[i] : 0.f;
+                }
                 uint32_t pk[2][4];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int i0 = 8 * h + 2 * e, ko = 16 * h + 2 * e;
-                        const float p0 = ko <= lim ? fast_exp2(fmaf(s[i0], a.c, nlse)) : 0.f;
-                        const float p1 = ko + 1 <= lim ? fast_exp2(fmaf(s[i0 + 1], a.c, nlse)) : 0.f;
-                        pk[h][e] = M::pack(p0 * (dp[i0] - Dq), p1 * (dp[i0 + 1] - Dq));
+                        const int i0 = 8 * h + 2 * e;
+                        pk[h][e] = M::pack(s[i0] * (dp[i0] - Dq), s[i0 + 1] * (dp[i0 + 1] - Dq));
                     }
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
@@ -276,6 +284,8 @@ struct BwdDq : BwdCommon<T, D> {
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[db] = M::mma(C::tr_frag(kb, lane, db, kc), ds, acc[db]);
                 }
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+                sched_mfma_reads<2 * DB, 2, 4 * DB - 4>();
             }
             bwd_barrier<0>();
         }
@@ -300,15 +310,21 @@ struct BwdDkv : BwdCommon<T, D> {
     static constexpr int NW = 8, GW = 4, THREADS = NW * 64;
     static constexpr int BKV = GW * 32;              // key rows per workgroup
     static constexpr int BQ = 32;                    // queries per streamed block
-    static constexpr int KV_B = 2 * BKV * ROWB;      // resident K then V tile
+    // The resident K and V tiles are read only row-wise (as B operands), so they use a
+    // padded row of CH + 1 chunks instead of the swizzle: sixteen consecutive rows at one
+    // chunk still fall on sixteen bank groups, and a lane's fragments for successive
+    // k-steps sit at fixed offsets from one address.
+    static constexpr int PROW = ROWB + 16;           // padded row bytes
+    static constexpr int KV_B = 2 * BKV * PROW;      // resident K then V tile
     static constexpr int BLK_B = BQ * ROWB;          // one Q or dO block
     static constexpr int STAGE_B = 2 * BLK_B + 256;  // Q, dO, then L (32 floats) and D (32 floats)
     static constexpr int RING_B = 2 * STAGE_B;       // two stages per group
     static constexpr int LDS_B = KV_B + 2 * RING_B;
     static constexpr int LOADS = 2 * BLK_B / 1024 / GW;  // Q/dO loads per wave and block
-    static constexpr int KV_LOADS = KV_B / 1024 / NW;
+    static constexpr int KV_LOADS = KV_B / 1024;     // 1 KiB loads of both tiles (any wave)
     static constexpr int PART_B = GW * DB * 16 * 64 * 4;  // one group's dK (or dV) partials, fp32
-    static_assert(LOADS * 1024 * GW == 2 * BLK_B && KV_LOADS * 1024 * NW == KV_B, "loads split evenly");
+    static_assert(LOADS * 1024 * GW == 2 * BLK_B && KV_LOADS * 1024 == KV_B && KV_LOADS % 2 == 0,
+                  "whole loads");
     static_assert(PART_B <= KV_B && PART_B <= 2 * RING_B, "partials fit in the freed LDS");
 
     static __device__ __forceinline__ void put_part(const f32x16_t (&acc)[DB], uint32_t base, int lane) {
@@ -358,7 +374,9 @@ struct BwdDkv : BwdCommon<T, D> {
         const int kv0 = kt * BKV;               // first key of the workgroup
         const int k0 = kv0 + 32 * wk, key = k0 + l32;
         const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
-        const uint32_t kres = lds0, vres = lds0 + BKV * ROWB, ring = lds0 + KV_B + grp * RING_B;
+        const uint32_t kres = lds0, ring = lds0 + KV_B + grp * RING_B;
+        // this lane's B-operand row of the resident tiles: key row 32 wk + l32, chunk g
+        const uint32_t kv_lane = kres + (32 * wk + l32) * PROW + 16 * g;
 
         f32x16_t dk[DB], dv[DB];
 #pragma unroll
@@ -367,15 +385,19 @@ struct BwdDkv : BwdCommon<T, D> {
             dv[b] = (f32x16_t){};
         }
 
-        // resident K and V rows kv0 .. kv0 + BKV - 1 (this wave's share of the loads)
-        {
-            constexpr int PER = BKV * ROWB / 1024;
+        // resident K and V rows kv0 .. kv0 + BKV - 1: 1 KiB loads w, w + NW, ...; slot s of a
+        // tile is row s / (CH + 1), chunk s % (CH + 1); the pad chunk CH loads chunk 0 again
 #pragma unroll
-            for (int t = 0; t < KV_LOADS; ++t) {
-                const int ch = w * KV_LOADS + t;
-                const bool isv = ch >= PER;
-                C::load_rows(isv ? Vh : Kh, kv0, N, isv ? vres : kres, ch % PER, 1, lane);
-            }
+        for (int t0 = 0; t0 < KV_LOADS; t0 += NW) {
+            const int t = __builtin_amdgcn_readfirstlane(t0 + w);
+            if (t >= KV_LOADS) break;
+            constexpr int PER = KV_LOADS / 2;  // loads per tile
+            const bool isv = t >= PER;
+            const int sl = (t % PER) * 64 + lane;
+            const int r = sl / (C::CH + 1), p = sl % (C::CH + 1);
+            const int src = min(kv0 + r, N - 1) - kv0;
+            dma_to_lds16((isv ? Vh : Kh) + (size_t)kv0 * ROWB, (uint32_t)src * ROWB + (p < C::CH ? p << 4 : 0),
+                         kres + (isv ? BKV * PROW : 0) + (t % PER) * 1024);
         }
         const int nqb = (N + BQ - 1) / BQ;
         const int qb0 = CAUSAL ? kv0 / BQ : 0;      // queries before kv0 see none of these keys
@@ -411,37 +433,46 @@ struct BwdDkv : BwdCommon<T, D> {
                 f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    s = M::mma(C::row_frag(qb, l32, g, cc), C::col_frag(kres, 32 * wk + l32, g, cc), s);
+                    s = M::mma(C::row_frag(qb, l32, g, cc),
+                               C::as_v8(*(const lds_u32x4_t *)(uintptr_t)(kv_lane + 32 * cc)), s);
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    dp = M::mma(C::row_frag(ob, l32, g, cc), C::col_frag(vres, 32 * wk + l32, g, cc), dp);
+                    dp = M::mma(C::row_frag(ob, l32, g, cc),
+                                C::as_v8(*(const lds_u32x4_t *)(uintptr_t)(kv_lane + BKV * PROW + 32 * cc)), dp);
+                // fragment reads run four ahead of the products that use them
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+                sched_mfma_reads<2 * DC, 2, 4 * DC - 4>();
                 // register i of half g holds query i BQ + 16 (i >> 3) + 8 g + (i & 7); lane = key
-                uint32_t pp[2][4], pd[2][4];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int qo = 16 * h + 8 * g;  // first query offset of these 8 registers
-                    const u32x4_t l0 = *(const lds_u32x4_t *)(uintptr_t)(lb + 4 * qo);
-                    const u32x4_t l1 = *(const lds_u32x4_t *)(uintptr_t)(lb + 4 * qo + 16);
-                    const u32x4_t d0 = *(const lds_u32x4_t *)(uintptr_t)(lb + 128 + 4 * qo);
-                    const u32x4_t d1 = *(const lds_u32x4_t *)(uintptr_t)(lb + 128 + 4 * qo + 16);
-                    const float Ls[8] = {__uint_as_float(l0[0]), __uint_as_float(l0[1]), __uint_as_float(l0[2]),
-                                         __uint_as_float(l0[3]), __uint_as_float(l1[0]), __uint_as_float(l1[1]),
-                                         __uint_as_float(l1[2]), __uint_as_float(l1[3])};
-                    const float Ds[8] = {__uint_as_float(d0[0]), __uint_as_float(d0[1]), __uint_as_float(d0[2]),
-                                         __uint_as_float(d0[3]), __uint_as_float(d1[0]), __uint_as_float(d1[1]),
-                                         __uint_as_float(d1[2]), __uint_as_float(d1[3])};
+                    const u32x4_t lv[2] = {*(const lds_u32x4_t *)(uintptr_t)(lb + 4 * qo),
+                                           *(const lds_u32x4_t *)(uintptr_t)(lb + 4 * qo + 16)};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        s[8 * h + e] = fast_exp2(fmaf(s[8 * h + e], a.c, -__uint_as_float(lv[e >> 2][e & 3]) * kLog2e));
+                }
+                // only blocks where some query does not see some key of the wave are masked
+                if ((CAUSAL && i * BQ < k0 + 31) || i * BQ + BQ > N) {
+#pragma unroll
+                    for (int ii = 0; ii < 16; ++ii) {
+                        const int qidx = i * BQ + 16 * (ii >> 3) + 8 * g + (ii & 7);
+                        s[ii] = qidx < N && (!CAUSAL || qidx >= key) ? s[ii] : 0.f;
+                    }
+                }
+                uint32_t pp[2][4], pd[2][4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int qo = 16 * h + 8 * g;
+                    const u32x4_t dv4[2] = {*(const lds_u32x4_t *)(uintptr_t)(lb + 128 + 4 * qo),
+                                            *(const lds_u32x4_t *)(uintptr_t)(lb + 128 + 4 * qo + 16)};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float p[2], ds[2];
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const int ii = 8 * h + 2 * e + t, qidx = i * BQ + qo + 2 * e + t;
-                            const bool vis = qidx < N && (!CAUSAL || qidx >= key);
-                            p[t] = vis ? fast_exp2(fmaf(s[ii], a.c, -Ls[2 * e + t] * kLog2e)) : 0.f;
-                            ds[t] = p[t] * (dp[ii] - Ds[2 * e + t]);
-                        }
-                        pp[h][e] = M::pack(p[0], p[1]);
-                        pd[h][e] = M::pack(ds[0], ds[1]);
+                        const int ii = 8 * h + 2 * e;
+                        const float D0 = __uint_as_float(dv4[e >> 1][(2 * e) & 3]);
+                        const float D1 = __uint_as_float(dv4[e >> 1][(2 * e + 1) & 3]);
+                        pp[h][e] = M::pack(s[ii], s[ii + 1]);
+                        pd[h][e] = M::pack(s[ii] * (dp[ii] - D0), s[ii + 1] * (dp[ii + 1] - D1));
                     }
                 }
 #pragma unroll
@@ -454,6 +485,8 @@ struct BwdDkv : BwdCommon<T, D> {
                         dk[db] = M::mma(C::tr_frag(qb, lane, db, kc), dS, dk[db]);
                     }
                 }
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+                sched_mfma_reads<4 * DB, 2, 8 * DB - 4>();
             }
             bwd_barrier<0>();
         }
