@@ -10,8 +10,10 @@ triangle mask, softmax over keys and the per-row log-sum-exp, following
 "Understand FlashAttention" (nothiny.github.io), sections "前向传播" and
 "附：数值稳定的logsumexp(L)推导", and "PyTorch profiling part 3: attention",
 section "朴素注意力" (naive attention); and its backward (dQ, dK, dV of a loss
-with gradient dO) from "Understand FlashAttention", section "反向传播".  This
-module only marshals arrays.
+with gradient dO) from "Understand FlashAttention", section "反向传播"; and the
+general-mask form (boolean or additive mask, unequal query and key lengths,
+safe softmax) from "PyTorch profiling part 3", sections "构建因果掩码" and
+"安全 softmax".  This module only marshals arrays.
 
 Pins (tests/test_oracle.py) tie it to facts the pages and the mathematics fix;
 every function here is pinned (none is "parity unpinned").
@@ -66,6 +68,9 @@ class OracleLib:
         lib.oracle_attn_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                             ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_bwd_f64.restype = ctypes.c_int
+        lib.oracle_attn_masked_f64.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, i64, i64, i64, i64,
+                                               i64, ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_masked_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -132,6 +137,46 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_bwd_f64 failed with status {rc}")
         return dq, dk, dv
 
+    def attn_masked(self, q, k, v, scale: float, causal: bool, mask=None, kind: str = "bool"):
+        """O [B, H, Nq, d], lse [B, H, Nq] with a general mask and Nq != Nk allowed.
+
+        q: [B, H, Nq, d]; k, v: [B, H, Nk, d].  mask: None, or an array broadcastable to
+        [B, H, Nq, Nk] whose leading two axes are B or 1: kind "bool" (nonzero = key visible,
+        turned into an additive 0 / -inf bias as the math backend does, "PyTorch profiling
+        part 3", section "构建因果掩码") or kind "add" (added to the scaled scores).
+        causal: bottom-right aligned lower triangle (key j visible iff j <= i + Nk - Nq).
+        Rows that see no key: o = 0, lse = -inf.
+        """
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+                or q.shape[3] != k.shape[3]:
+            raise ValueError("q [B, H, Nq, d], k and v [B, H, Nk, d] expected")
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        bias_p, sb, sh = None, 0, 0
+        if mask is not None:
+            m = _f64(mask) if kind == "add" else None
+            if kind == "bool":
+                mb = np.asarray(mask.detach().cpu().numpy() if hasattr(mask, "detach") else mask)
+                m = np.where(mb != 0, 0.0, -np.inf)
+            elif kind != "add":
+                raise ValueError("kind must be 'bool' or 'add'")
+            if m.ndim != 4 or m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) \
+                    or m.shape[1] not in (1, H):
+                raise ValueError(f"mask of shape {m.shape} does not broadcast to {(B, H, Nq, Nk)}")
+            m = np.ascontiguousarray(m, dtype=np.float64)
+            sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * Nk
+            sh = 0 if m.shape[1] == 1 else Nq * Nk
+            bias_p = m
+        o = np.empty((B, H, Nq, d), dtype=np.float64)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self.lib.oracle_attn_masked_f64(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(bias_p) if bias_p is not None else None, sb, sh,
+            _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale), int(bool(causal)))
+        if rc:
+            raise RuntimeError(f"oracle_attn_masked_f64 failed with status {rc}")
+        return o, lse
+
 
 def _f64(x) -> np.ndarray:
     """Exact widening of a torch tensor or array to a C-contiguous fp64 array."""
@@ -172,3 +217,7 @@ def attn_dense(q, k, scale: float, causal: bool):
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool):
     return default().attn_bwd(q, k, v, dout, scale, causal)
+
+
+def attn_masked(q, k, v, scale: float, causal: bool, mask=None, kind: str = "bool"):
+    return default().attn_masked(q, k, v, scale, causal, mask, kind)

@@ -30,8 +30,8 @@
  *     attention, steps 1-3);
  *   - a row with every key masked (plain softmax would give 0/0) yields
  *     o = 0 and lse = -inf, the "safe softmax" reading of that page's section
- *     "安全 softmax".  The library's boundary (equal query and key lengths,
- *     diagonal kept) never produces such a row.
+ *     "安全 softmax".  The plain forward (equal query and key lengths,
+ *     diagonal kept) never produces such a row; the masked one below can.
  *
  * The backward (oracle_attn_bwd_f64, below) follows the same page's section
  * "反向传播" and recomputes each softmax row from the definition.
@@ -303,6 +303,93 @@ int oracle_attn_bwd_f64(const double *q, const double *k, const double *v,
         }
         free(P);
         free(dP);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Attention with a general mask and unequal query and key lengths, all heads.
+ *
+ *   q       : [B, H, Nq, d];  k, v : [B, H, Nk, d]   row-major fp64
+ *   o       : [B, H, Nq, d] (written);  lse : [B, H, Nq] (written)
+ *   bias    : NULL (no mask) or an additive mask; element (b, h, i, j) sits at
+ *             bias[b * sb + h * sh + i * Nk + j] (sb = 0 or sh = 0 broadcasts
+ *             one mask over batches or heads).  -inf hides key j from query i;
+ *             finite values are added to the scaled score.
+ *   causal  : key j is visible to query i iff j <= i + (Nk - Nq): the lower
+ *             triangle anchored at the bottom-right corner, so the Nq queries
+ *             are the last Nq positions of the key sequence.
+ *
+ * "PyTorch profiling part 3: attention", section "朴素注意力": scores = q k^T,
+ * times the scale, masked entries -inf, softmax over keys, times v; section
+ * "构建因果掩码": a mask is applied as an additive bias of 0 or -inf after the
+ * scaling; section "安全 softmax": a row whose every entry is -inf would give
+ * 0/0, and the safe softmax returns zeros there, so such a row gets o = 0 and
+ * lse = -inf.  The log-sum-exp is that of the scaled, biased, masked row
+ * ("Understand FlashAttention", appendix "附：数值稳定的logsumexp(L)推导").
+ */
+int oracle_attn_masked_f64(const double *q, const double *k, const double *v,
+                           const double *bias, int64_t sb, int64_t sh,
+                           double *o, double *lse, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t d, double scale,
+                           int causal)
+{
+    if (!q || !k || !v || !o || !lse) return 1;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    const int64_t rows = B * H * Nq;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Nk * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!s) continue;
+            const int64_t head = r / Nq, i = r % Nq;
+            const int64_t b = head / H, h = head % H;
+            const double *q_i = q + r * d;
+            const double *kh = k + head * Nk * d, *vh = v + head * Nk * d;
+            const double *bias_i = bias ? bias + b * sb + h * sh + i * Nk : NULL;
+            double *o_i = o + r * d;
+            /* steps 1-3: scaled scores, plus the additive mask, causal entries -inf */
+            for (int64_t j = 0; j < Nk; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += q_i[c] * kh[j * d + c];
+                s[j] = dot * scale;
+                if (bias_i)
+                    s[j] += bias_i[j];
+                if (causal && j > i + (Nk - Nq))
+                    s[j] = -INFINITY;
+            }
+            /* step 4: stable softmax; a row with no visible key is all zeros */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Nk; ++j)
+                if (s[j] > m)
+                    m = s[j];
+            for (int64_t c = 0; c < d; ++c)
+                o_i[c] = 0.0;
+            if (m == -INFINITY) {
+                lse[r] = -INFINITY;
+                continue;
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+            /* step 5: out = P v */
+            for (int64_t j = 0; j < Nk; ++j) {
+                const double w = s[j] / l;
+                for (int64_t c = 0; c < d; ++c)
+                    o_i[c] += w * vh[j * d + c];
+            }
+            lse[r] = m + log(l);
+        }
+        free(s);
     }
     return failed ? 2 : 0;
 }

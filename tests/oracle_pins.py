@@ -20,6 +20,10 @@ Sources (pages cited by title and section):
         - "构建因果掩码": the causal mask is the lower triangle (tril), key j <= query i
   [FA]  "反向传播": dV = P^T dO, dP = dO V^T, dS = P o (dP - rowsum(P o dP)),
         dQ = dS K, dK = dS^T Q (the backward pins below; S carries the scale)
+  [PT]  "构建因果掩码" (a mask enters as an additive 0 / -inf bias after scaling) and
+        "安全 softmax" (a row with every entry -inf yields zeros, not 0/0): the
+        general-mask pins below; for Nq != Nk the causal triangle is anchored at the
+        bottom-right corner (the queries are the last Nq positions of the keys)
 """
 from __future__ import annotations
 
@@ -440,6 +444,150 @@ def pin_bwd_heads_independent(orc):
                                g[b:b + 1, hh:hh + 1], 0.5, True)
             for full, part in zip((dq, dk, dv), one):
                 assert np.array_equal(full[b, hh], part[0, 0])
+
+
+# ---------------------------------------------------------------- general masks
+
+def pin_masked_reduces_to_plain(orc):
+    """No mask and Nq = Nk: the same numbers as the plain (pinned) forward."""
+    rng = np.random.default_rng(40)
+    for causal in (False, True):
+        q, k, v = rng.standard_normal((3, 2, 3, 9, 5))
+        o, lse = orc.attn_masked(q, k, v, 0.4, causal)
+        o2, lse2 = orc.attn_fwd(q, k, v, 0.4, causal)
+        _close(o, o2, 1e-15, f"no mask O causal={causal}")
+        _close(lse, lse2, 1e-15, f"no mask lse causal={causal}")
+
+
+def pin_masked_tril_is_causal(orc):
+    """A boolean lower-triangle mask ([PT] 构建因果掩码: ones -> tril) and the equivalent
+    additive 0 / -inf bias both equal the plain causal forward."""
+    rng = np.random.default_rng(41)
+    q, k, v = rng.standard_normal((3, 2, 2, 10, 4))
+    tril = np.tril(np.ones((10, 10), dtype=np.uint8))[None, None]
+    o_ref, lse_ref = orc.attn_fwd(q, k, v, 0.7, True)
+    o, lse = orc.attn_masked(q, k, v, 0.7, False, tril, "bool")
+    _close(o, o_ref, 1e-15, "tril bool O")
+    _close(lse, lse_ref, 1e-15, "tril bool lse")
+    bias = np.where(tril != 0, 0.0, -np.inf)
+    o, lse = orc.attn_masked(q, k, v, 0.7, False, bias, "add")
+    _close(o, o_ref, 1e-15, "tril additive O")
+    _close(lse, lse_ref, 1e-15, "tril additive lse")
+
+
+def pin_masked_bottom_right(orc):
+    """Nq < Nk, causal: the Nq queries are the last Nq positions, so they equal the last
+    Nq rows of the square causal problem whose earlier query rows are arbitrary.
+    Nq > Nk: the first Nq - Nk queries see no key (o = 0, lse = -inf) and the last Nk
+    rows equal the square causal problem on them."""
+    rng = np.random.default_rng(42)
+    B, H, d = 1, 2, 6
+    for Nq, Nk in ((1, 9), (4, 11), (11, 11)):
+        q_full, k, v = rng.standard_normal((3, B, H, Nk, d))
+        q = q_full[:, :, Nk - Nq:]
+        o_ref, lse_ref = orc.attn_fwd(q_full, k, v, 0.5, True)
+        o, lse = orc.attn_masked(q, k, v, 0.5, True)
+        _close(o, o_ref[:, :, Nk - Nq:], 1e-15, f"bottom-right O {Nq, Nk}")
+        _close(lse, lse_ref[:, :, Nk - Nq:], 1e-15, f"bottom-right lse {Nq, Nk}")
+    Nq, Nk = 7, 3
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((2, B, H, Nk, d))
+    o, lse = orc.attn_masked(q, k, v, 0.5, True)
+    assert np.all(o[:, :, :Nq - Nk] == 0.0) and np.all(lse[:, :, :Nq - Nk] == -np.inf)
+    o_ref, lse_ref = orc.attn_fwd(q[:, :, Nq - Nk:], k, v, 0.5, True)
+    _close(o[:, :, Nq - Nk:], o_ref, 1e-15, "Nq > Nk O")
+    _close(lse[:, :, Nq - Nk:], lse_ref, 1e-15, "Nq > Nk lse")
+
+
+def pin_masked_safe_softmax(orc):
+    """[PT] 安全 softmax: a row with every key hidden gives o = 0 and lse = -inf exactly
+    (no NaN); the other rows equal the problem without those rows."""
+    rng = np.random.default_rng(43)
+    B, H, Nq, Nk, d = 1, 2, 6, 8, 5
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((2, B, H, Nk, d))
+    mask = rng.random((B, H, Nq, Nk)) < 0.6
+    mask[:, :, [1, 4]] = False
+    mask[:, :, [0, 2, 3, 5], 0] = True
+    o, lse = orc.attn_masked(q, k, v, 0.8, False, mask, "bool")
+    assert np.all(o[:, :, [1, 4]] == 0.0) and np.all(lse[:, :, [1, 4]] == -np.inf)
+    keep = [0, 2, 3, 5]
+    o2, lse2 = orc.attn_masked(q[:, :, keep], k, v, 0.8, False, mask[:, :, keep], "bool")
+    _close(o[:, :, keep], o2, 1e-15, "unmasked rows O")
+    _close(lse[:, :, keep], lse2, 1e-15, "unmasked rows lse")
+    assert np.isfinite(o).all()
+
+
+def pin_masked_single_key(orc):
+    """One visible key per row: the softmax weight is exactly 1, so o_i = v_j and
+    lse_i = scale q_i . k_j + bias_ij."""
+    rng = np.random.default_rng(44)
+    B, H, Nq, Nk, d = 1, 1, 5, 7, 3
+    q = rng.integers(-3, 4, (B, H, Nq, d)).astype(np.float64)
+    k, v = rng.integers(-3, 4, (2, B, H, Nk, d)).astype(np.float64)
+    pick = rng.integers(0, Nk, Nq)
+    bias = np.full((1, 1, Nq, Nk), -np.inf)
+    bias[0, 0, np.arange(Nq), pick] = 0.25 * np.arange(Nq)
+    o, lse = orc.attn_masked(q, k, v, 0.5, False, bias, "add")
+    for i, j in enumerate(pick):
+        assert np.array_equal(o[0, 0, i], v[0, 0, j])
+        assert lse[0, 0, i] == 0.5 * float(q[0, 0, i] @ k[0, 0, j]) + 0.25 * i
+
+
+def pin_masked_row_constant_bias(orc):
+    """A finite bias constant along each row leaves P and O unchanged ([FA] 数值稳定的
+    Softmax: shift invariance) and adds the constant to lse."""
+    rng = np.random.default_rng(45)
+    B, H, Nq, Nk, d = 2, 2, 5, 9, 4
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((2, B, H, Nk, d))
+    c = rng.standard_normal((B, H, Nq, 1)) * 3
+    for causal in (False, True):
+        o, lse = orc.attn_masked(q, k, v, 0.6, causal, np.broadcast_to(c, (B, H, Nq, Nk)), "add")
+        o2, lse2 = orc.attn_masked(q, k, v, 0.6, causal)
+        _close(o, o2, 1e-13, f"row bias O causal={causal}")
+        _close(lse, lse2 + c[..., 0], 1e-13, f"row bias lse causal={causal}")
+
+
+def pin_masked_broadcast(orc):
+    """A mask shared over batches or heads equals the same mask repeated."""
+    rng = np.random.default_rng(46)
+    B, H, Nq, Nk, d = 2, 3, 4, 6, 5
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((2, B, H, Nk, d))
+    for shape in ((1, 1), (B, 1), (1, H)):
+        m = rng.standard_normal(shape + (Nq, Nk))
+        o, lse = orc.attn_masked(q, k, v, 0.3, True, m, "add")
+        o2, lse2 = orc.attn_masked(q, k, v, 0.3, True, np.broadcast_to(m, (B, H, Nq, Nk)).copy(), "add")
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    mb = rng.standard_normal((B, 1, Nq, Nk))
+    mh = rng.standard_normal((1, H, Nq, Nk))
+    o, _ = orc.attn_masked(q, k, v, 0.3, False, mb, "add")
+    o2, _ = orc.attn_masked(q, k, v, 0.3, False, mh, "add")
+    assert np.max(np.abs(o - o2)) > 1e-3
+
+
+def pin_masked_torch_sdpa(orc):
+    """torch's CPU fp64 SDPA with a boolean or float attn_mask and torch.logsumexp of the
+    biased scores ([PT] math backend; its bool mask marks the keys that take part)."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(47)
+    for (B, H, Nq, Nk, d) in [(1, 1, 1, 5, 8), (2, 2, 9, 13, 16), (1, 2, 33, 20, 64)]:
+        q = rng.standard_normal((B, H, Nq, d))
+        k, v = rng.standard_normal((2, B, H, Nk, d))
+        mb = rng.random((B, H, Nq, Nk)) < 0.7
+        mb[..., rng.integers(0, Nk)] = True
+        bias = rng.standard_normal((1, H, Nq, Nk))
+        scale = 1.0 / math.sqrt(d)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        for kind, m, tm, sb in (("bool", mb, torch.from_numpy(mb), s.masked_fill(~torch.from_numpy(mb), float("-inf"))),
+                                ("add", bias, torch.from_numpy(bias), s + torch.from_numpy(bias))):
+            o, lse = orc.attn_masked(q, k, v, scale, False, m, kind)
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=scale)
+            _close(o, ref.numpy(), 1e-12, f"sdpa masked O {kind} {B,H,Nq,Nk,d}")
+            _close(lse, torch.logsumexp(sb, dim=-1).numpy(), 1e-12, f"sdpa masked lse {kind}")
 
 
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -49,6 +49,14 @@ MUTANTS = [
      "for (int64_t c = 0; c < d; ++c) dot += do_i[c] * kh[j * d + c];"),
     ("bwd_mask_drops_diagonal", "const int64_t nvis = causal ? i + 1 : N;", "const int64_t nvis = causal ? i : N;"),
     ("bwd_not_normalised", "for (int64_t j = 0; j < nvis; ++j) P[j] /= l;", "for (int64_t j = 0; j < nvis; ++j) P[j] /= (l + 0.5);"),
+    ("masked_top_left_causal", "if (causal && j > i + (Nk - Nq))", "if (causal && j > i)"),
+    ("masked_bias_subtracted", "s[j] += bias_i[j];", "s[j] -= bias_i[j];"),
+    ("masked_bias_ignored", "s[j] += bias_i[j];", "s[j] += 0.0 * bias_i[j];"),
+    ("masked_no_safe_softmax", "lse[r] = -INFINITY;\n                continue;", "lse[r] = -INFINITY;"),
+    ("masked_strides_swapped", "bias + b * sb + h * sh + i * Nk", "bias + h * sb + b * sh + i * Nk"),
+    ("masked_wrong_value_row", "o_i[c] += w * vh[j * d + c];", "o_i[c] += w * vh[c];"),
+    ("masked_not_normalised", "const double w = s[j] / l;", "const double w = s[j];"),
+    ("masked_diagonal_hidden", "if (causal && j > i + (Nk - Nq))", "if (causal && j >= i + (Nk - Nq))"),
     ("bwd_scores_unscaled", "P[j] = dot * scale;\n                    if (P[j] > m) m = P[j];",
      "P[j] = dot;\n                    if (P[j] > m) m = P[j];"),
 ]
