@@ -2,8 +2,8 @@
 
 Every step of the forward and backward runs in the HIP library; this module
 checks the tensors, allocates the outputs with torch and passes raw device
-pointers and torch's current HIP stream to ``attn_fwd`` and ``attn_bwd``
-(declared in include/attn.h).
+pointers and torch's current HIP stream to ``attn_fwd``, ``attn_fwd_masked``,
+``attn_mask_pack`` and ``attn_bwd`` (declared in include/attn.h).
 There is no fallback: a missing library or a failed call raises.
 """
 from __future__ import annotations
@@ -43,6 +43,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float,
                                ci, ci, vp]
         L.attn_bwd.restype = ci
+        ll = ctypes.c_longlong
+        L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, ll, ll, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float,
+                                      ci, ci, vp]
+        L.attn_fwd_masked.restype = ci
+        L.attn_mask_pack.argtypes = [vp, vp, ll, ci, vp]
+        L.attn_mask_pack.restype = ci
         L.attn_strerror.argtypes = [ci]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
@@ -64,6 +70,19 @@ def attn_fwd_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: in
     """Raw call with integer device addresses; returns the status code."""
     return int(lib().attn_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
                               causal, dtype, stream))
+
+
+def attn_fwd_masked_ptr(q: int, k: int, v: int, mask_bits: int | None, mask_stride_b: int,
+                        mask_stride_h: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int, d: int,
+                        scale: float, causal: int, dtype: int, stream: int) -> int:
+    """Raw call with integer device addresses (mask_bits None or 0: no mask)."""
+    return int(lib().attn_fwd_masked(q, k, v, mask_bits or None, mask_stride_b, mask_stride_h, o, lse,
+                                     B, H, Nq, Nk, d, ctypes.c_float(scale), causal, dtype, stream))
+
+
+def attn_mask_pack_ptr(mask: int, bits: int, rows: int, Nk: int, stream: int) -> int:
+    """Raw call with integer device addresses; returns the status code."""
+    return int(lib().attn_mask_pack(mask, bits, rows, Nk, stream))
 
 
 def attn_bwd_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
@@ -124,6 +143,101 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
                           B, H, N, d, float(scale), int(bool(causal)), code, stream)
     if st != ATTN_OK:
         raise AttnError(st, strerror(st))
+    return out, lse
+
+
+def pack_mask(mask):
+    """Packs a boolean mask [Bm, Hm, Nq, Nk] (torch.bool or uint8, contiguous, on a HIP
+    device; nonzero = key visible) into the bit format of attn_fwd_masked: an int64
+    tensor [Bm, Hm, Nq, ceil(Nk / 64)] whose bit j % 64 of word j / 64 is key j.  The
+    packing runs on the GPU (attn_mask_pack) on torch's current stream."""
+    import torch
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a torch.Tensor")
+    if mask.device.type != "cuda":
+        raise ValueError(f"mask must be on a HIP device, got {mask.device}")
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise TypeError(f"mask must be torch.bool or torch.uint8, got {mask.dtype}")
+    if mask.dim() != 4 or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous [Bm, Hm, Nq, Nk] tensor")
+    Bm, Hm, Nq, Nk = mask.shape
+    rows = Bm * Hm * Nq
+    bits = torch.empty((Bm, Hm, Nq, (Nk + 63) // 64), dtype=torch.int64, device=mask.device)
+    with torch.cuda.device(mask.device):
+        stream = torch.cuda.current_stream(mask.device).cuda_stream
+        st = attn_mask_pack_ptr(mask.data_ptr(), bits.data_ptr(), rows, Nk, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, strerror(st), "attn_mask_pack")
+    return bits
+
+
+def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | None = None,
+                    mask_bits=None, out=None, lse=None):
+    """Attention forward with unequal query and key lengths and an optional mask.
+
+    q: [B, H, Nq, d]; k, v: [B, H, Nk, d]; one HIP device, one dtype, contiguous.
+    mask: None, or a boolean mask [Bm, Hm, Nq, Nk] (Bm in {1, B}, Hm in {1, H}; true =
+    visible), packed on the GPU first; or mask_bits: an already packed mask (see
+    pack_mask).  causal: keys j > i + Nk - Nq are hidden as well.  Returns (o, lse):
+    o like q, lse float32 [B, H, Nq]; a row that sees no key gets o = 0, lse = -inf.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q [B, H, Nq, d] and k, v [B, H, Nk, d] expected, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    code = _dtype_code(q)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if mask is not None and mask_bits is not None:
+        raise ValueError("pass mask or mask_bits, not both")
+    if mask is not None:
+        if not isinstance(mask, torch.Tensor) or mask.device != q.device:
+            raise ValueError("mask must be a tensor on q's device")
+        mask_bits = pack_mask(mask)
+    sb = sh = 0
+    mptr = None
+    if mask_bits is not None:
+        W = (Nk + 63) // 64
+        if not isinstance(mask_bits, torch.Tensor) or mask_bits.dtype != torch.int64 \
+                or mask_bits.dim() != 4 or not mask_bits.is_contiguous() or mask_bits.device != q.device:
+            raise ValueError("mask_bits must be a contiguous int64 [Bm, Hm, Nq, ceil(Nk/64)] tensor on q's device")
+        Bm, Hm = mask_bits.shape[:2]
+        if Bm not in (1, B) or Hm not in (1, H) or tuple(mask_bits.shape[2:]) != (Nq, W):
+            raise ValueError(f"mask of shape {tuple(mask_bits.shape)} does not match "
+                             f"[{B} or 1, {H} or 1, {Nq}, {W}]")
+        sb = 0 if Bm == 1 else Hm * Nq * W
+        sh = 0 if Hm == 1 else Nq * W
+        mptr = mask_bits.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_masked_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, sb, sh, out.data_ptr(),
+                                 lse.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)), code,
+                                 stream)
+    if st != ATTN_OK:
+        raise AttnError(st, strerror(st), "attn_fwd_masked")
     return out, lse
 
 

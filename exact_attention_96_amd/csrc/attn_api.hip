@@ -33,13 +33,13 @@ hipError_t launch(Kernel *kernel, int grid, int threads, int lds_bytes, hipStrea
                            static_cast<size_t>(lds_bytes), stream);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_f32(const FwdArgs &a, int bh, hipStream_t stream) {
-    constexpr int QW = attn::F32Fwd<D, CAUSAL>::QW;
+    typedef attn::F32Fwd<D, CAUSAL, MASK> K;
     FwdArgs b = a;
-    b.n_qtiles = (a.N + QW - 1) / QW;
-    b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
-    return launch(&attn::attn_fwd_f32_kernel<D, CAUSAL>, b.total, attn::F32Fwd<D, CAUSAL>::THREADS, 0, stream, b);
+    b.n_qtiles = (a.Nq + K::QW - 1) / K::QW;
+    b.total = bh * b.n_qtiles;  // bounded by the check in fwd_core
+    return launch(&attn::attn_fwd_f32_kernel<D, CAUSAL, MASK>, b.total, K::THREADS, 0, stream, b);
 }
 
 // Opt a kernel in to its dynamic LDS size, once per device (devices 0..63; others
@@ -57,32 +57,57 @@ hipError_t opt_in_lds(const void *kernel, int lds_bytes) {
     return r;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int MODE>
 hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
-    typedef attn::MfmaFwd<T, D, CAUSAL> K;
+    typedef attn::MfmaFwd<T, D, CAUSAL, MODE> K;
     FwdArgs b = a;
-    b.n_qtiles = (a.N + K::BR - 1) / K::BR;
-    b.total = bh * b.n_qtiles;  // bounded by the check in attn_fwd
+    b.n_qtiles = (a.Nq + K::BR - 1) / K::BR;
+    b.total = bh * b.n_qtiles;  // bounded by the check in fwd_core
     constexpr int lds_bytes = K::LDS_B;
     const hipError_t attr =
-        opt_in_lds<K>(reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>), lds_bytes);
+        opt_in_lds<K>(reinterpret_cast<const void *>(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL, MODE>), lds_bytes);
     if (attr != hipSuccess) return attr;
-    return launch(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL>, b.total, K::THREADS, lds_bytes, stream, b);
+    return launch(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL, MODE>, b.total, K::THREADS, lds_bytes, stream, b);
 }
 
-template <int D, bool CAUSAL>
+// MODE: attn::kFwdPlain / kFwdOffset / kFwdBits (the fp32 kernel only tells masked
+// from unmasked)
+template <int D, bool CAUSAL, int MODE>
 hipError_t dispatch_dtype(const FwdArgs &a, int bh, int dtype, hipStream_t stream) {
     switch (dtype) {
-        case ATTN_F32: return launch_f32<D, CAUSAL>(a, bh, stream);
-        case ATTN_F16: return launch_mfma<_Float16, D, CAUSAL>(a, bh, stream);
-        default: return launch_mfma<__bf16, D, CAUSAL>(a, bh, stream);
+        case ATTN_F32: return launch_f32<D, CAUSAL, MODE == attn::kFwdBits>(a, bh, stream);
+        case ATTN_F16: return launch_mfma<_Float16, D, CAUSAL, MODE>(a, bh, stream);
+        default: return launch_mfma<__bf16, D, CAUSAL, MODE>(a, bh, stream);
     }
 }
 
+// Variant choice: a mask needs kFwdBits; a causal offset Nk - Nq that is not a
+// multiple of 32 lets a wave's diagonal cross a unit boundary (kFwdOffset);
+// everything else, including every equal-length problem, runs kFwdPlain.
 template <int D>
-hipError_t dispatch_causal(const FwdArgs &a, int bh, int causal, int dtype, hipStream_t stream) {
-    return causal ? dispatch_dtype<D, true>(a, bh, dtype, stream)
-                  : dispatch_dtype<D, false>(a, bh, dtype, stream);
+hipError_t dispatch_mode(const FwdArgs &a, int bh, int causal, int dtype, hipStream_t stream) {
+    if (a.mask)
+        return causal ? dispatch_dtype<D, true, attn::kFwdBits>(a, bh, dtype, stream)
+                      : dispatch_dtype<D, false, attn::kFwdBits>(a, bh, dtype, stream);
+    if (!causal) return dispatch_dtype<D, false, attn::kFwdPlain>(a, bh, dtype, stream);
+    if (a.off % 32 != 0) return dispatch_dtype<D, true, attn::kFwdOffset>(a, bh, dtype, stream);
+    return dispatch_dtype<D, true, attn::kFwdPlain>(a, bh, dtype, stream);
+}
+
+// Packs a byte mask [rows, Nk] into bits [rows, ceil(Nk / 64)]: one wave per
+// 64-bit word, each lane reading one key's byte; the wave's ballot is the word.
+__global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t *mask, uint64_t *bits, long long words,
+                                                             int Nk, int w_per_row) {
+    const int lane = threadIdx.x & 63;
+    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long n_waves = (long long)gridDim.x * 4;
+    for (long long i = wave; i < words; i += n_waves) {
+        const long long r = i / w_per_row;
+        const int key = (int)(i - r * w_per_row) * 64 + lane;
+        const bool on = key < Nk && mask[r * Nk + key] != 0;
+        const uint64_t word = __builtin_amdgcn_ballot_w64(on);
+        if (lane == 0) bits[i] = word;
+    }
 }
 
 // Backward: D_i = dO_i . O_i, then dQ and dK/dV (independent of each other).
@@ -120,28 +145,39 @@ hipError_t bwd_causal(const BwdArgs &a, int bh, int causal, int dtype, hipStream
     return causal ? bwd_dtype<D, true>(a, bh, dtype, stream) : bwd_dtype<D, false>(a, bh, dtype, stream);
 }
 
-}  // namespace
-
-extern "C" ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                        int N, int d, float scale, int causal, int dtype, hipStream_t stream) {
+// Checks and launch shared by attn_fwd and attn_fwd_masked (mask may be NULL).
+int fwd_core(const void *q, const void *k, const void *v, const void *mask, long long msb, long long msh, void *o,
+             float *lse, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+             hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
-    if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_EINVAL;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!isfinite(scale)) return ATTN_EINVAL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return ATTN_EINVAL;
     const uint64_t elt = dtype == ATTN_F32 ? 4 : 2;
-    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
-    const uint64_t tbytes = rows * (uint64_t)d * elt;
-    const uint64_t lbytes = rows * 4;
-    if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) || overlaps(o, tbytes, v, tbytes) ||
-        overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
-        overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes))
+    const uint64_t rows_q = (uint64_t)B * (uint64_t)H * (uint64_t)Nq;
+    const uint64_t rows_k = (uint64_t)B * (uint64_t)H * (uint64_t)Nk;
+    const uint64_t qb = rows_q * (uint64_t)d * elt, kb = rows_k * (uint64_t)d * elt;
+    const uint64_t lbytes = rows_q * 4;
+    const uint64_t mw = ((uint64_t)Nk + 63) / 64;  // mask words per row
+    uint64_t mbytes = 0;
+    if (mask) {
+        if (!aligned(mask, 8) || msb < 0 || msh < 0) return ATTN_EINVAL;
+        // one past the last word read: (B-1) sb + (H-1) sh + Nq mw (checked in 64 bits)
+        if ((uint64_t)msb > (1ull << 40) || (uint64_t)msh > (1ull << 40)) return ATTN_EUNSUPPORTED;
+        mbytes = ((uint64_t)(B - 1) * (uint64_t)msb + (uint64_t)(H - 1) * (uint64_t)msh + (uint64_t)Nq * mw) * 8;
+    }
+    if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) || overlaps(lse, lbytes, q, qb) ||
+        overlaps(lse, lbytes, k, kb) || overlaps(lse, lbytes, v, kb) || overlaps(lse, lbytes, o, qb))
         return ATTN_EINVAL;
+    if (mask && (overlaps(o, qb, mask, mbytes) || overlaps(lse, lbytes, mask, mbytes))) return ATTN_EINVAL;
     if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
     // the smallest query tile is 32 rows; the 1-D grid holds at most INT32_MAX workgroups
-    if ((uint64_t)B * (uint64_t)H * (((uint64_t)N + 31) / 32) > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
+    if ((uint64_t)B * (uint64_t)H * (((uint64_t)Nq + 31) / 32) > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
+    // a head's mask rows are addressed with 32-bit byte offsets
+    if (mask && (uint64_t)Nq * mw * 8 > (uint64_t)UINT32_MAX) return ATTN_EUNSUPPORTED;
 
     FwdArgs a;
     a.q = q;
@@ -149,14 +185,50 @@ extern "C" ATTN_API int attn_fwd(const void *q, const void *k, const void *v, vo
     a.v = v;
     a.o = o;
     a.lse = lse;
-    a.N = N;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.off = Nk - Nq;
     a.n_qtiles = 0;
     a.total = 0;
     a.c = (float)((double)scale * 1.4426950408889634073599);
+    a.mask = static_cast<const uint64_t *>(mask);
+    a.mask_sb = msb;
+    a.mask_sh = msh;
+    a.mask_w = (int)mw;
+    a.H = H;
     const int bh = B * H;
-    const hipError_t err = d == 64 ? dispatch_causal<64>(a, bh, causal, dtype, stream)
-                                   : dispatch_causal<128>(a, bh, causal, dtype, stream);
+    const hipError_t err = d == 64 ? dispatch_mode<64>(a, bh, causal, dtype, stream)
+                                   : dispatch_mode<128>(a, bh, causal, dtype, stream);
     return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+extern "C" ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                                 int N, int d, float scale, int causal, int dtype, hipStream_t stream) {
+    return fwd_core(q, k, v, nullptr, 0, 0, o, lse, B, H, N, N, d, scale, causal, dtype, stream);
+}
+
+extern "C" ATTN_API int attn_fwd_masked(const void *q, const void *k, const void *v, const void *mask_bits,
+                                        long long mask_stride_b, long long mask_stride_h, void *o, float *lse, int B,
+                                        int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                                        hipStream_t stream) {
+    return fwd_core(q, k, v, mask_bits, mask_stride_b, mask_stride_h, o, lse, B, H, Nq, Nk, d, scale, causal, dtype,
+                    stream);
+}
+
+extern "C" ATTN_API int attn_mask_pack(const void *mask, void *bits, long long rows, int Nk, hipStream_t stream) {
+    if (!mask || !bits || rows < 1 || Nk < 1) return ATTN_EINVAL;
+    if (!aligned(bits, 8)) return ATTN_EINVAL;
+    const uint64_t w = ((uint64_t)Nk + 63) / 64;
+    if ((uint64_t)rows > (1ull << 40) / w) return ATTN_EUNSUPPORTED;
+    const uint64_t words = (uint64_t)rows * w;
+    if (overlaps(bits, words * 8, mask, (uint64_t)rows * (uint64_t)Nk)) return ATTN_EINVAL;
+    const uint64_t blocks = (words + 3) / 4;
+    const int grid = (int)(blocks < 65536 ? blocks : 65536);
+    const hipError_t e = launch(&attn_mask_pack_kernel, grid, 256, 0, stream, static_cast<const uint8_t *>(mask),
+                                static_cast<uint64_t *>(bits), (long long)words, Nk, (int)w);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
 extern "C" ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

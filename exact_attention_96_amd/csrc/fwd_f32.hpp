@@ -15,7 +15,8 @@
 
 namespace attn {
 
-template <int D, bool CAUSAL>
+// MASK: keys are also hidden by the caller's bit mask (FwdArgs::mask).
+template <int D, bool CAUSAL, bool MASK = false>
 struct F32Fwd {
     static constexpr int QW = 32;  // query rows per workgroup
     static constexpr int BK = 32;  // keys per LDS block
@@ -26,15 +27,15 @@ struct F32Fwd {
         __shared__ __attribute__((aligned(16))) float k_lds[BK * D];
         __shared__ __attribute__((aligned(16))) float v_lds[BK * D];
 
-        const int N = a.N;
+        const int Nq = a.Nq, Nk = a.Nk, off = CAUSAL ? a.off : 0;
         const int logical = xcd_contiguous(blockIdx.x, a.total);
         const int bh = logical / a.n_qtiles;
         const int t = logical - bh * a.n_qtiles;
         const int qt = CAUSAL ? a.n_qtiles - 1 - t : t;
-        const size_t head = (size_t)bh * (size_t)N * D;
+        const size_t head = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
         const float *Qh = static_cast<const float *>(a.q) + head;
-        const float *Kh = static_cast<const float *>(a.k) + head;
-        const float *Vh = static_cast<const float *>(a.v) + head;
+        const float *Kh = static_cast<const float *>(a.k) + headk;
+        const float *Vh = static_cast<const float *>(a.v) + headk;
 
         const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
         const int q0 = qt * QW;
@@ -43,20 +44,29 @@ struct F32Fwd {
         float qv[DH], acc[DH];
 #pragma unroll
         for (int e = 0; e < DH; ++e) {
-            qv[e] = qrow < N ? Qh[(size_t)qrow * D + g * DH + e] : 0.f;
+            qv[e] = qrow < Nq ? Qh[(size_t)qrow * D + g * DH + e] : 0.f;
             acc[e] = 0.f;
         }
         float m = -INFINITY, l = 0.f;
 
-        const int n_kv_all = (N + BK - 1) / BK;
-        const int n_kv = CAUSAL ? min(n_kv_all, (q0 + QW - 1) / BK + 1) : n_kv_all;
+        // the row's mask words (MASK); rows past the end read row Nq - 1
+        const uint64_t *mrow = nullptr;
+        if (MASK) {
+            const int b = bh / a.H, hh = bh - b * a.H;
+            mrow = a.mask + (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh +
+                   (size_t)min(qrow, Nq - 1) * (size_t)a.mask_w;
+        }
+        // causal: the workgroup's last row sees keys up to its index + off
+        const int n_kv_all = (Nk + BK - 1) / BK;
+        const int last_key = min(q0 + QW, Nq) - 1 + off;
+        const int n_kv = CAUSAL ? (last_key < 0 ? 0 : min(n_kv_all, last_key / BK + 1)) : n_kv_all;
         for (int j = 0; j < n_kv; ++j) {
             const int k0 = j * BK;
             __syncthreads();
             for (int idx = lane; idx < BK * D / 4; idx += THREADS) {
                 const int r = idx / (D / 4), cc = idx % (D / 4);
                 f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-                if (k0 + r < N) {
+                if (k0 + r < Nk) {
                     kx = *reinterpret_cast<const f32x4_t *>(Kh + (size_t)(k0 + r) * D + cc * 4);
                     vx = *reinterpret_cast<const f32x4_t *>(Vh + (size_t)(k0 + r) * D + cc * 4);
                 }
@@ -65,6 +75,8 @@ struct F32Fwd {
             }
             __syncthreads();
 
+            // BK = 32 keys from k0 (a multiple of 32) lie in one mask word
+            const uint32_t mbits = MASK ? (uint32_t)(mrow[k0 / 64] >> (k0 % 64)) : 0xffffffffu;
             float s[BK];
             float mx = -INFINITY;
 #pragma unroll
@@ -74,7 +86,7 @@ struct F32Fwd {
                 for (int e = 0; e < DH; ++e) part = fmaf(qv[e], k_lds[jj * D + g * DH + e], part);
                 float x = (part + __shfl_xor(part, 32)) * a.c;
                 const int key = k0 + jj;
-                if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
+                if (key >= Nk || (CAUSAL && key > qrow + off) || !((mbits >> jj) & 1u)) x = -INFINITY;
                 s[jj] = x;
                 mx = fmaxf(mx, x);
             }
@@ -98,20 +110,20 @@ struct F32Fwd {
             }
         }
 
-        if (qrow < N) {
-            const float inv = 1.f / l;
+        if (qrow < Nq) {  // a row that saw no key (l = 0, m = -inf): O = 0, lse = -inf
+            const float inv = l > 0.f ? 1.f / l : 0.f;
             float *Oh = static_cast<float *>(a.o) + head + (size_t)qrow * D + g * DH;
 #pragma unroll
             for (int e = 0; e < DH; ++e) Oh[e] = acc[e] * inv;
-            if (g == 0) a.lse[(size_t)bh * N + qrow] = (m + fast_log2(l)) * kLn2;
+            if (g == 0) a.lse[(size_t)bh * Nq + qrow] = (m + fast_log2(l)) * kLn2;
         }
     }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64)
 void attn_fwd_f32_kernel(FwdArgs a) {
-    F32Fwd<D, CAUSAL>::run(a);
+    F32Fwd<D, CAUSAL, MASK>::run(a);
 }
 
 }  // namespace attn

@@ -63,10 +63,18 @@ struct FwdArgs {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int N;           // sequence length
-    int n_qtiles;    // ceil(N / BR)
+    int Nq, Nk;      // query and key sequence lengths
+    int off;         // causal diagonal offset: key j is visible to query i iff j <= i + off (Nk - Nq)
+    int n_qtiles;    // ceil(Nq / BR)
     int total;       // B * H * n_qtiles
     float c;         // scale * log2(e)
+    // Optional bit mask (kernels instantiated with MASK only): bit j % 64 of word
+    // j / 64 of row i is 1 iff key j is visible to query i.  Head (b, h) starts at
+    // word b * mask_sb + h * mask_sh; rows are mask_w = ceil(Nk / 64) words apart.
+    const uint64_t *mask;
+    long long mask_sb, mask_sh;
+    int mask_w;
+    int H;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -146,12 +154,35 @@ __device__ __forceinline__ void dma_to_lds16(const void *base, uint32_t voff, ui
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
+// The same with 4 bytes per lane (LDS at lds + 4 * lane).  base must be
+// wave-uniform; it is passed through readfirstlane so that it lives in SGPRs.
+__device__ __forceinline__ void dma_to_lds4(const void *base, uint32_t voff, uint32_t lds) {
+    // (readfirstlane returns a signed int: widen through uint32_t, or an address whose
+    // bit 31 is set would sign-extend into the upper word)
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint64_t u = (uint64_t)lo | ((uint64_t)hi << 32);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
+                 "s"(reinterpret_cast<const void *>(u)), "s"(lds)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-template <typename T, int D, bool CAUSAL>
+// Kernel variants.  kFwdPlain: at most one unit per wave needs the masked
+// softmax (equal lengths, or a causal offset Nk - Nq that is a multiple of 32):
+// straight-line code, the register budget of the hot path.  kFwdOffset: any
+// causal offset; the wave's masked units (one or two) run in a loop.  kFwdBits:
+// keys are also hidden by a caller's bit mask (FwdArgs::mask), read per unit
+// through an LDS ring of its own that rides in the K/V load groups; every unit
+// takes the masked softmax.
+constexpr int kFwdPlain = 0, kFwdOffset = 1, kFwdBits = 2;
+
+template <typename T, int D, bool CAUSAL, int MODE = kFwdPlain>
 struct MfmaFwd {
+    static constexpr bool MASK = MODE == kFwdBits;
     static constexpr int NW = 8;                     // waves per workgroup, two per SIMD
     static constexpr int BR = NW * 32;               // query rows per workgroup, 32 per wave
     static constexpr int BU = 64;                    // keys per unit (one matrix phase)
@@ -161,9 +192,13 @@ struct MfmaFwd {
     static constexpr int ROWB = D * 2;               // bytes per K/V row
     static constexpr int UNIT_B = BU * ROWB;         // bytes per K or V unit
     static constexpr int V_BASE = STAGES * UNIT_B;   // V ring follows the K ring
-    static constexpr int LDS_B = 2 * STAGES * UNIT_B;
+    static constexpr int MUNIT_B = BR * 8;           // mask bits of one unit: a 64-bit word per row
+    static constexpr int M_BASE = 2 * STAGES * UNIT_B;  // mask ring follows the V ring
+    static constexpr int LDS_B = M_BASE + (MASK ? STAGES * MUNIT_B : 0);
     static constexpr int LOADS = BU * CH / 64 / NW;  // 16-byte-per-lane DMA loads per wave, unit and tensor
-    static constexpr int GROUP = 2 * LOADS;          // DMA loads per wave in one load group
+    static constexpr int KVLOADS = 2 * LOADS;        // K and V loads per wave in one load group
+    static constexpr int GROUP = KVLOADS + (MASK ? 1 : 0);  // plus one 4-byte mask load per wave
+    static_assert(!MASK || MUNIT_B == NW * 64 * 4, "one 4-byte mask load per lane covers a unit");
     static constexpr int DB = D / 32;                // 32-row blocks of O^T
     static constexpr int DC = D / 16;                // k-steps of the first product
     static constexpr float kSumBound = 65536.0f;  // 2^SUM_LOG2 with SUM_LOG2 = 16
@@ -190,7 +225,8 @@ struct MfmaFwd {
         uint32_t kaddr[DC];      // LDS address of this lane's K fragment for k-step cc (stage 0)
         uint32_t vaddr[DB];      // LDS address of this lane's V^T fragment for d block db (stage 0)
         float c;                 // scale * log2(e), >= 0
-        int r0, N, l32, g;       // first row of the wave, sequence length, lane coordinates
+        int r0, Nk, off, l32, g; // first row of the wave, key length, causal offset, lane coordinates
+        uint32_t mrow;           // LDS offset of the lane's row in a mask stage (MASK)
     };
 
     // ------------------------------------------------------------ building blocks
@@ -245,8 +281,8 @@ struct MfmaFwd {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST, 0);
         sched_mfma_reads<NS, PER, NV - FIRST>();
         constexpr int NP = 4 * DB;       // P V MFMAs per unit
-        constexpr int CHUNK = NP / GROUP;
-        static_assert(NP % GROUP == 0, "P V MFMAs split evenly around the loads");
+        constexpr int CHUNK = NP / KVLOADS;
+        static_assert(NP % KVLOADS == 0, "P V MFMAs split evenly around the loads");
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int h = j / (2 * DB), kc = (j / DB) % 2, db = j % DB;
@@ -264,19 +300,38 @@ struct MfmaFwd {
     // Keys of a unit are visible to this lane's row up to a per-lane limit:
     // accumulator register i of half h holds the key at offset key_off(h, i) from
     // the unit start k0, and that key is visible iff key_off(h, i) <= lim(k0), with
-    // lim = min(row, N - 1) - k0 - 8 g (causal) or N - 1 - k0 - 8 g.
+    // lim = min(row + off, Nk - 1) - k0 - 8 g (causal) or Nk - 1 - k0 - 8 g.
     static __device__ __forceinline__ constexpr int key_off(int h, int i) { return 32 * h + (i & 7) + 16 * (i >> 3); }
     static __device__ __forceinline__ int vis_limit(const State &S, int k0) {
-        const int last = CAUSAL ? min(S.r0 + S.l32, S.N - 1) : S.N - 1;
+        const int last = CAUSAL ? min(S.r0 + S.l32 + S.off, S.Nk - 1) : S.Nk - 1;
         return last - k0 - 8 * S.g;
     }
+
+    // MASK: visibility of the lane's 32 scores of a unit as bits, bit 16 h + i for
+    // register i of half h: the caller's mask bits (row word of the unit in LDS at
+    // moff) and the position limit.  Register i of half h is key 16 r + 8 g + (i & 7)
+    // with r = 2 h + (i >> 3), i.e. byte 2 r + g of the row word; key offsets grow
+    // with the bit index, so the position limit keeps a prefix of the bits.
+    static __device__ __forceinline__ uint32_t visible_bits(const State &S, int k0, uint32_t moff) {
+        const u32x2_t wd = *(const __attribute__((address_space(3))) u32x2_t *)(uintptr_t)(S.mrow + moff);
+        const uint32_t lo = wd[0] >> (8 * S.g), hi = wd[1] >> (8 * S.g);
+        const uint32_t bits = (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi & 0xff0000u) << 8);
+        const int lim = vis_limit(S, k0);
+        int n = 0;  // registers whose key offset is <= lim: a prefix of the bit order
+#pragma unroll
+        for (int r = 0; r < 4; ++r) n += min(max(lim - 16 * r + 1, 0), 8);
+        const uint32_t pos = n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+        return bits & pos;
+    }
+    static __device__ __forceinline__ bool vis_bit(uint32_t vm, int b) { return (vm >> b) & 1u; }
 
     // p = 2^(s c - m) for the unit starting at key k0 against the current reference
     // m, rounded to T in the B-operand layout; returns this lane's fp32 sum of p.
     template <bool MASKED>
-    static __device__ __forceinline__ float exps(const State &S, const f32x16_t (&s)[2], Packed &pk, int k0) {
+    static __device__ __forceinline__ float exps(const State &S, const f32x16_t (&s)[2], Packed &pk, int k0,
+                                                 uint32_t vm) {
         const float nm = S.m_ref == -INFINITY ? 0.f : -S.m_ref;
-        const int lim = MASKED ? vis_limit(S, k0) : 0;
+        const int lim = MASKED && !MASK ? vis_limit(S, k0) : 0;
         float rs = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -287,7 +342,10 @@ struct MfmaFwd {
                     const int i0 = 8 * kc + 2 * e;
                     float p0 = fast_exp2(fmaf(s[h][i0], S.c, nm));
                     float p1 = fast_exp2(fmaf(s[h][i0 + 1], S.c, nm));
-                    if (MASKED) {
+                    if (MASK) {
+                        p0 = vis_bit(vm, 16 * h + i0) ? p0 : 0.f;
+                        p1 = vis_bit(vm, 16 * h + i0 + 1) ? p1 : 0.f;
+                    } else if (MASKED) {
                         p0 = key_off(h, i0) <= lim ? p0 : 0.f;
                         p1 = key_off(h, i0 + 1) <= lim ? p1 : 0.f;
                     }
@@ -303,17 +361,24 @@ struct MfmaFwd {
     // range and the unit is done.  Otherwise (a row whose max grew well past m) the
     // row max of the unit is taken, m moves to it, O~ and the row sum are rescaled,
     // and the exponentials are taken again.  The first unit of a tile (FIRST: m is
-    // still -inf, O~ and the sum are zero) starts from its row max directly.
+    // still -inf, O~ and the sum are zero) starts from its row max directly.  In the
+    // looping variants (a caller's mask, or a row's first unit inside the loop) a
+    // unit whose rows still have the reference -inf also takes the row max, which
+    // starts the reference (it stays -inf while the row has seen no visible key).
+    // moff: LDS offset of the unit's mask stage (MASK only).
     template <bool MASKED, bool FIRST>
-    static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0) {
+    static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0, uint32_t moff = 0) {
+        const uint32_t vm = MASK ? visible_bits(S, k0, moff) : 0u;
         auto move_reference = [&](bool rescale) {
-            const int lim = MASKED ? vis_limit(S, k0) : 0;
+            const int lim = MASKED && !MASK ? vis_limit(S, k0) : 0;
             float mx = -INFINITY;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, MASKED ? (key_off(h, i) <= lim ? s[h][i] : -INFINITY) : s[h][i]);
+                    mx = fmaxf(mx, MASK     ? (vis_bit(vm, 16 * h + i) ? s[h][i] : -INFINITY)
+                                   : MASKED ? (key_off(h, i) <= lim ? s[h][i] : -INFINITY)
+                                            : s[h][i]);
             mx = lane_swap32_max(mx);
             const float mt = mx == -INFINITY ? -INFINITY : mx * S.c;
             const float m_new = fmaxf(S.m_ref, mt);
@@ -330,12 +395,12 @@ struct MfmaFwd {
         float rs;
         if (FIRST) {
             move_reference(false);
-            rs = exps<MASKED>(S, s, pk, k0);
+            rs = exps<MASKED>(S, s, pk, k0, vm);
         } else {
-            rs = exps<MASKED>(S, s, pk, k0);
-            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
+            rs = exps<MASKED>(S, s, pk, k0, vm);
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound) || (MODE != kFwdPlain && S.m_ref == -INFINITY))) {
                 move_reference(true);
-                rs = exps<MASKED>(S, s, pk, k0);
+                rs = exps<MASKED>(S, s, pk, k0, vm);
             }
         }
         S.lsum += rs;
@@ -355,7 +420,7 @@ struct MfmaFwd {
     static __device__ void run(const FwdArgs &a) {
         extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-        const int N = a.N;
+        const int Nq = a.Nq, Nk = a.Nk, off = CAUSAL ? a.off : 0;
         // Work order.  The 8 XCDs take block indices round robin, each with its own L2.
         // Causal: longest tiles first, so that the dispatcher always starts the longest
         // remaining tile.  When B*H is a multiple of 16, XCD x serves the heads congruent
@@ -383,10 +448,10 @@ struct MfmaFwd {
             bh = logical / a.n_qtiles;
             qt = logical - bh * a.n_qtiles;
         }
-        const size_t head = (size_t)bh * (size_t)N * D;
+        const size_t head = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
         const uint16_t *Qh = static_cast<const uint16_t *>(a.q) + head;
-        const char *Kh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head);
-        const char *Vh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head);
+        const char *Kh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + headk);
+        const char *Vh = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + headk);
 
         const int tid = threadIdx.x;
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -397,7 +462,8 @@ struct MfmaFwd {
 
         State S;
         S.r0 = qt * BR + 64 * (w & 3) + 32 * (w >> 2);
-        S.N = N;
+        S.Nk = Nk;
+        S.off = off;
         S.l32 = l32;
         S.g = g;
         // A negative scale is applied as -|c| by negating Q (exact), so c >= 0 below.
@@ -409,11 +475,11 @@ struct MfmaFwd {
         }
 
         // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its row q
-        // (rows past the end read row N-1 and are zeroed).
+        // (rows past the end read row Nq-1 and are zeroed).
         {
             const int q = S.r0 + l32;
-            const uint32_t keep = q < N ? 0xffffffffu : 0u;
-            const uint16_t *qrow = Qh + (size_t)min(q, N - 1) * D + g * 8;
+            const uint32_t keep = q < Nq ? 0xffffffffu : 0u;
+            const uint16_t *qrow = Qh + (size_t)min(q, Nq - 1) * D + g * 8;
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) {
                 u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + cc * 16);
@@ -454,20 +520,42 @@ struct MfmaFwd {
             kld[i] = ((r & ~31) | swap_bits23(r & 31)) * ROWB + ((p ^ kswz(r)) << 4);
             vld[i] = r * ROWB + ((p ^ vswz(r)) << 4);
         }
+        // Mask loads (MASK): lane fills bytes 4 (lane & 1) .. +3 of the unit word of
+        // workgroup row (64 w + lane) / 2, stored densely (8 bytes per row) in LDS.  The
+        // lane's source offset is recomputed per load (registers are scarce in the loop).
+        const uint64_t *Mh = nullptr;
+        if (MASK) {
+            const int b = bh / a.H, hh = bh - b * a.H;
+            Mh = a.mask + (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh;
+            S.mrow = lds0 + M_BASE + (uint32_t)(S.r0 - qt * BR + l32) * 8u;
+        }
+        auto mask_src = [&]() -> uint32_t {
+            const int q = min(qt * BR + ((w * 64 + (l32 + 32 * g)) >> 1), Nq - 1);
+            return (uint32_t)q * (uint32_t)a.mask_w * 8u + 4u * (uint32_t)(l32 & 1);
+        };
 
-        // Units of BU keys this workgroup and this wave need.
-        const int n_units = (N + BU - 1) / BU;
-        const int nu_wg = CAUSAL ? min(n_units, (min(qt * BR + BR, N) - 1) / BU + 1) : n_units;
-        const int nu = S.r0 >= N ? 0 : (CAUSAL ? min(n_units, (S.r0 + 31) / BU + 1) : n_units);
+        // Units of BU keys this workgroup and this wave need: causal rows see keys up
+        // to row + off (none when that is negative).  A workgroup loads at least one
+        // unit so that every load is in bounds; waves without keys only pass barriers.
+        auto units_to = [&](int last_key) { return last_key < 0 ? 0 : last_key / BU + 1; };
+        const int n_units = (Nk + BU - 1) / BU;
+        const int nu_wg = CAUSAL ? max(1, min(n_units, units_to(min(qt * BR + BR, Nq) - 1 + off))) : n_units;
+        const int nu = S.r0 >= Nq ? 0 : (CAUSAL ? min(n_units, units_to(min(S.r0 + 31, Nq - 1) + off)) : n_units);
+        // The first nm units are visible to every row of the wave (no caller mask, keys
+        // below the first row's diagonal and the sequence end) and take the unmasked
+        // softmax; the rest of the wave's units (at least the last one) are masked.
+        const int n_full = CAUSAL ? (min(S.r0 + off, Nk - 1) + 1) / BU : Nk / BU;
+        const int nm = MASK ? 0 : max(0, min(nu - 1, n_full));
+        // kFwdPlain is only launched where nu - nm <= 1 for every wave
 
         // Load j of a unit (16 bytes per lane) into a ring stage.  Rows past the end of
-        // the sequence read row N - 1 (their scores are masked); the clamp is a no-op
+        // the sequence read row Nk - 1 (their scores are masked); the clamp is a no-op
         // for full units.
         auto load_one = [&](const char *src_head, int lds_off, uint32_t ld, int unit, int j) {
             const int k0 = unit * BU;
             const char *src = src_head + (size_t)k0 * ROWB;
             const uint32_t dst = lds0 + lds_off + (w * LOADS + j) * 1024;
-            const uint32_t last = (uint32_t)min(N - 1 - k0, BU - 1) * ROWB;
+            const uint32_t last = (uint32_t)min(Nk - 1 - k0, BU - 1) * ROWB;
             const uint32_t off = min(ld & ~(uint32_t)(ROWB - 1), last) + (ld & (ROWB - 1));
             dma_to_lds16(src, off, dst);
         };
@@ -475,16 +563,24 @@ struct MfmaFwd {
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) load_one(src_head, lds_off, ld[j], unit, j);
         };
-        // Load group i (i >= 1): K of unit i into stage i mod STAGES and V of unit i - 1
-        // into stage (i - 1) mod STAGES.  Groups past the last unit repeat the last unit
+        // Load group i (i >= 1): K of unit i into stage i mod STAGES, V of unit i - 1
+        // into stage (i - 1) mod STAGES and (MASK) the mask bits of unit i - 1 into mask
+        // stage (i - 1) mod STAGES.  Groups past the last unit repeat the last unit
         // into stages nobody reads any more, so that every group is GROUP loads and
         // the waits below are constant counts.  issue_part(i, j) issues load j of the
-        // group (K loads first, then V loads).
+        // group (K loads first, then V loads, then the mask load).
         auto issue_part = [&](int i, int j) {
             if (j < LOADS)
                 load_one(Kh, (i % STAGES) * UNIT_B, kld[j], min(i, nu_wg - 1), j);
-            else
+            else if (j < KVLOADS)
                 load_one(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld[j - LOADS], min(i - 1, nu_wg - 1), j - LOADS);
+            else
+                dma_to_lds4(Mh + min(i - 1, nu_wg - 1), mask_src(), lds0 + M_BASE + ((i - 1) % STAGES) * MUNIT_B + w * 256);
+        };
+        // the mask load of a group goes first in its step, the K/V loads are spread
+        // over the P V MFMAs by gemm
+        auto issue_mask = [&](int i) {
+            if (MASK) issue_part(i, KVLOADS);
         };
         auto issue = [&](int i) {
 #pragma unroll
@@ -532,6 +628,7 @@ struct MfmaFwd {
         };
         auto plain_step = [&](auto st, int u) {
             constexpr int ST = decltype(st)::value;  // u mod STAGES
+            issue_mask(u + STAGES - 1);
             gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((ST + 1) % STAGES) * UNIT_B);
@@ -547,9 +644,10 @@ struct MfmaFwd {
         kload(S, kf, 0);
         if (lag) barrier_end();
         int u = 0;
-        if (nu > 1) {
-            // unit 0 (plain, first of the tile), then the plain units up to nu - 2,
+        if (!MASK && nm > 0) {
+            // unit 0 (plain, first of the tile), then the plain units up to nm - 1,
             // unrolled by four from unit 1 so that the ring stage is an immediate
+            issue_mask(STAGES - 1);
             gemm(S, s, pk, kf, (STAGES - 1) * UNIT_B, [&](int j) { issue_part(STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, 1 * UNIT_B);
@@ -557,13 +655,14 @@ struct MfmaFwd {
             pin_soft();
             barrier_end();
             u = 1;
-            for (; u + STAGES < nu; u += STAGES) {
+            for (; u + STAGES <= nm; u += STAGES) {
                 plain_step(std::integral_constant<int, 1>(), u);
                 plain_step(std::integral_constant<int, 2>(), u + 1);
                 plain_step(std::integral_constant<int, 3>(), u + 2);
                 plain_step(std::integral_constant<int, 0>(), u + 3);
             }
-            for (; u + 1 < nu; ++u) {  // remaining plain steps, ring stage from u
+            for (; u < nm; ++u) {  // remaining plain steps, ring stage from u
+                issue_mask(u + STAGES - 1);
                 gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
                 barrier_mid();
                 kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
@@ -572,17 +671,31 @@ struct MfmaFwd {
                 barrier_end();
             }
         }
-        if (nu > 0) {  // step nu - 1 (masked softmax) and step nu (P V of the last unit)
+        auto masked_step = [&]() {
+            issue_mask(u + STAGES - 1);
             gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
-            if (u == 0)
+            if (MODE != kFwdPlain)  // a reference still at -inf takes the row max
+                soft<true, false>(S, s, pk, u * BU, (u % STAGES) * MUNIT_B);
+            else if (u == 0)
                 soft<true, true>(S, s, pk, u * BU);
             else
                 soft<true, false>(S, s, pk, u * BU);
             pin_soft();
             barrier_end();
+        };
+        // masked steps nm .. nu - 1: every unit with a caller's mask; one or two where
+        // the causal diagonal of the wave's 32 rows may cross a unit boundary; one in
+        // kFwdPlain
+        if (MODE != kFwdPlain) {
+            for (; u < nu; ++u) masked_step();
+        } else if (u < nu) {
+            masked_step();
             ++u;
+        }
+        if (nu > 0) {  // step nu: P V of the last unit (u = nu)
+            issue_mask(u + STAGES - 1);
             gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
             barrier_mid();
             barrier_end();
@@ -598,14 +711,15 @@ struct MfmaFwd {
         // to this workgroup only while the workgroup runs.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-        // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2.  Register i of block b is
+        // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2; a row that saw no key
+        // (l = 0, m = -inf) gets O = 0 and lse = -inf.  Register i of block b is
         // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q, so the two lane halves
         // of a row hold alternate groups of 4 columns.  One exchange between them (lane ^ 32,
         // same row) gives every lane 8 consecutive columns: 16-byte stores, half as many
         // store instructions as storing each lane's own groups of 4.
         const int q = S.r0 + l32;
         const float ltot = lane_swap32_add(S.lsum);
-        const float inv = 1.f / ltot;
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         auto partner = [&](uint32_t x) -> uint32_t {  // x of lane ^ 32
             const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
             return g ? r[0] : r[1];
@@ -626,20 +740,20 @@ struct MfmaFwd {
                 const u32x2_t give = g ? mine[0] : mine[1];
                 const u32x2_t got = {partner(give[0]), partner(give[1])};
                 const u32x2_t lo = g ? got : mine[0], hi = g ? mine[1] : got;
-                if (q < N) {
+                if (q < Nq) {
                     uint16_t *dst = static_cast<uint16_t *>(a.o) + head + (size_t)q * D + b * 32 + 8 * (k + g);
                     *reinterpret_cast<u32x4_t *>(dst) = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
                 }
             }
-        if (q < N && g == 0) a.lse[(size_t)bh * N + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
+        if (q < Nq && g == 0) a.lse[(size_t)bh * Nq + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
     }
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_mfma_kernel(FwdArgs a) {
-    static_assert(MfmaFwd<T, D, CAUSAL>::THREADS == 512, "launch bounds");
-    MfmaFwd<T, D, CAUSAL>::run(a);
+    static_assert(MfmaFwd<T, D, CAUSAL, MODE>::THREADS == 512, "launch bounds");
+    MfmaFwd<T, D, CAUSAL, MODE>::run(a);
 }
 
 }  // namespace attn

@@ -113,3 +113,52 @@ def random_grad(B: int, H: int, N: int, d: int, dtype: str, seed: int, std: floa
     g.manual_seed(seed)
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     return (torch.randn((B, H, N, d), dtype=torch.float32, generator=g) * std).to(dt)
+
+
+def random_qkv_lens(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int, std: float = 1.0):
+    """Q [B, H, Nq, d] and K, V [B, H, Nk, d] (CPU, `dtype`): drawn in the order Q, K, V
+    from one seeded generator as randn * std, then rounded to the dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), dtype=torch.float32, generator=g) * std
+    k = torch.randn((B, H, Nk, d), dtype=torch.float32, generator=g) * std
+    v = torch.randn((B, H, Nk, d), dtype=torch.float32, generator=g) * std
+    dt = DTYPES[dtype]
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+def random_mask(kind: str, Bm: int, Hm: int, Nq: int, Nk: int, seed: int, **kw) -> torch.Tensor:
+    """A boolean mask [Bm, Hm, Nq, Nk] (CPU; True = key visible) of a given pattern:
+
+    "bernoulli"  each entry visible with probability kw["p"] (default 0.5);
+    "window"     key j visible to query i iff i + Nk - Nq - kw["w"] < j <= i + Nk - Nq
+                 (a sliding window of w keys ending at the bottom-right diagonal);
+    "padding"    per (b, h) a random key length L in [1, Nk]: key j visible iff j < L
+                 (a padded batch);
+    "blocks"     64 x 64 blocks visible with probability kw["p"] (default 0.3), the rest
+                 hidden (block-sparse);
+    "empty_rows" bernoulli(0.5) with a random tenth of the rows hidden entirely.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (Bm, Hm, Nq, Nk)
+    if kind == "bernoulli":
+        return torch.rand(shape, generator=g) < kw.get("p", 0.5)
+    if kind == "window":
+        i = torch.arange(Nq).view(Nq, 1) + (Nk - Nq)
+        j = torch.arange(Nk).view(1, Nk)
+        m = (j <= i) & (j > i - kw["w"])
+        return m.expand(shape).contiguous()
+    if kind == "padding":
+        lens = torch.randint(1, Nk + 1, (Bm, Hm, 1, 1), generator=g)
+        return (torch.arange(Nk).view(1, 1, 1, Nk) < lens).expand(shape).contiguous()
+    if kind == "blocks":
+        nb = ((Nq + 63) // 64, (Nk + 63) // 64)
+        blk = torch.rand((Bm, Hm) + nb, generator=g) < kw.get("p", 0.3)
+        m = blk.repeat_interleave(64, dim=2).repeat_interleave(64, dim=3)
+        return m[:, :, :Nq, :Nk].contiguous()
+    if kind == "empty_rows":
+        m = torch.rand(shape, generator=g) < 0.5
+        rows = torch.rand((Bm, Hm, Nq, 1), generator=g) < 0.1
+        return (m & ~rows).contiguous()
+    raise ValueError(f"unknown mask kind {kind!r}")

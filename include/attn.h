@@ -49,8 +49,8 @@ typedef enum {
     ATTN_EHIP = 3          /* the HIP runtime reported an error at launch */
 } attn_status_t;
 
-/* Version of this ABI; bumped on any incompatible change. */
-#define ATTN_ABI_VERSION 1
+/* Version of this ABI; bumped when entry points change or are added. */
+#define ATTN_ABI_VERSION 2
 
 /*
  * attn_fwd — attention forward for B*H independent heads.
@@ -95,6 +95,73 @@ typedef enum {
 ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                       int B, int H, int N, int d, float scale, int causal, int dtype,
                       hipStream_t stream);
+
+/*
+ * attn_fwd_masked — attention forward with unequal query and key lengths and
+ * an optional boolean mask, for B*H independent heads.
+ *
+ * The mask follows "PyTorch profiling part 3: attention" (Hugging Face blog),
+ * section "构建因果掩码": a boolean matrix whose false entries become -inf
+ * scores after scaling (equivalently an additive 0 / -inf bias), combined with
+ * the causal triangle; a query row whose every key is hidden gets o = 0 and
+ * lse = -inf (the "safe softmax" reading of that page's section "安全 softmax",
+ * where the plain softmax of such a row would be 0/0).  With Nq != Nk the
+ * causal triangle is anchored at the bottom-right corner: the queries are the
+ * last Nq of the Nk positions, so key j is visible to query i iff
+ * j <= i + Nk - Nq (for Nq = Nk this is attn_fwd's mask).
+ *
+ * Arguments
+ *   q        device pointer, [B, H, Nq, d] contiguous of `dtype`; read only.
+ *   k, v     device pointers, [B, H, Nk, d] contiguous of `dtype`; read only.
+ *   mask_bits  NULL (no mask) or a device pointer to 64-bit words, 8-byte
+ *            aligned, as written by attn_mask_pack: the mask of head (b, h) is
+ *            Nq rows of ceil(Nk / 64) words starting at word
+ *            b * mask_stride_b + h * mask_stride_h; bit j % 64 of word j / 64 of
+ *            row i is 1 iff key j is visible to query i.  A stride of 0 shares
+ *            one mask across that axis.  Read only.
+ *   mask_stride_b, mask_stride_h  word strides, >= 0 (ignored without a mask).
+ *   o        device pointer, [B, H, Nq, d] contiguous of `dtype`; written.
+ *   lse      device pointer, [B, H, Nq] contiguous fp32; written.
+ *   B, H, Nq, Nk  batch, heads, query and key lengths, each >= 1.
+ *   d, scale, dtype, stream  as in attn_fwd.
+ *   causal   0: only the mask hides keys; 1: also keys j > i + Nk - Nq.
+ *
+ * Arithmetic, reproducibility, ownership and concurrency: as attn_fwd.  o and
+ * lse must not overlap q, k, v, the mask words read or each other.
+ *
+ * Errors are returned synchronously and nothing is launched on error:
+ *   ATTN_EINVAL       as attn_fwd (with Nq, Nk in place of N); a mask not
+ *                     8-byte aligned or a negative stride; o or lse overlapping
+ *                     the mask words.
+ *   ATTN_EUNSUPPORTED as attn_fwd; a head's mask larger than 4 GiB; a stride
+ *                     above 2^40.
+ *   ATTN_EHIP         as attn_fwd.
+ */
+ATTN_API int attn_fwd_masked(const void *q, const void *k, const void *v, const void *mask_bits,
+                             long long mask_stride_b, long long mask_stride_h, void *o, float *lse,
+                             int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                             int dtype, hipStream_t stream);
+
+/*
+ * attn_mask_pack — packs a boolean mask into the bit format of attn_fwd_masked.
+ *
+ * Arguments
+ *   mask     device pointer, [rows, Nk] contiguous bytes; nonzero = visible
+ *            ("PyTorch profiling part 3: attention", section "构建因果掩码":
+ *            true entries keep their score).  Read only.
+ *   bits     device pointer, [rows, ceil(Nk / 64)] 64-bit words, 8-byte aligned;
+ *            written: bit j % 64 of word j / 64 of row r = (mask[r, j] != 0);
+ *            bits past Nk are 0.
+ *   rows, Nk  >= 1.
+ *   stream   HIP stream the work is enqueued on.
+ *
+ * The packed mask can be reused by any number of attn_fwd_masked calls.
+ * Errors: ATTN_EINVAL (NULL pointer, rows or Nk < 1, bits misaligned, bits
+ * overlapping mask), ATTN_EUNSUPPORTED (more than 2^40 words), ATTN_EHIP
+ * (launch failure).  Asynchronous like attn_fwd.
+ */
+ATTN_API int attn_mask_pack(const void *mask, void *bits, long long rows, int Nk,
+                            hipStream_t stream);
 
 /*
  * attn_bwd — gradients of attention for B*H independent heads.

@@ -19,7 +19,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_strerror"]
+    assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_fwd_masked",
+                                  "attn_mask_pack", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,3 +126,55 @@ def test_bwd_outputs_right_after_inputs_are_fine():
     # dq placed right after dout (tensor bytes 2*3*100*64*2) does not overlap it.
     nbytes = 2 * 3 * 100 * 64 * 2
     assert call_bwd(dq=DO + nbytes, dtype=9) == ea.ATTN_EINVAL  # rejected for the dtype only
+
+
+# attn_fwd_masked and attn_mask_pack: host checks only (fake addresses, nothing launched).
+MB = 11 << 40
+GOOD_M = dict(q=Q, k=K, v=V, mask=MB, sb=0, sh=0, o=O, lse=L, B=2, H=3, Nq=100, Nk=300, d=64,
+              scale=0.125, causal=1, dtype=2, stream=0)
+M_ORDER = ["q", "k", "v", "mask", "sb", "sh", "o", "lse", "B", "H", "Nq", "Nk", "d", "scale",
+           "causal", "dtype", "stream"]
+
+
+def call_m(**kw):
+    a = dict(GOOD_M)
+    a.update(kw)
+    return ea.attn_fwd_masked_ptr(*(a[n] for n in M_ORDER))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+    dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(Nk=-3), dict(d=0),
+    dict(dtype=3), dict(causal=2), dict(scale=float("nan")),
+    dict(q=Q + 8), dict(k=K + 4), dict(o=O + 2), dict(lse=L + 1), dict(mask=MB + 4),
+    dict(sb=-1), dict(sh=-5),
+    dict(o=Q), dict(o=K + 16), dict(lse=V + 64), dict(lse=O + 16),
+    dict(o=MB), dict(lse=MB + 8 * 5 * 99),   # inside the mask words read (Nq rows of 5 words)
+    dict(o=V - 16),                          # o ends inside v (v holds Nk rows)
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_masked_invalid_arguments(kw):
+    assert call_m(**kw) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(B=65536, H=65536, Nq=1, Nk=1, d=64),
+                                dict(sb=1 << 41), dict(Nq=1 << 20, Nk=1 << 20)])
+def test_masked_unsupported(kw):
+    assert call_m(**kw) == ea.ATTN_EUNSUPPORTED
+
+
+def test_masked_without_mask_ignores_strides():
+    # no mask: the strides are not examined (a bad dtype is what is reported)
+    assert call_m(mask=0, sb=-1, sh=-1, dtype=9) == ea.ATTN_EINVAL
+
+
+def test_masked_lse_right_after_mask_is_fine_to_check():
+    # the mask spans (B-1) sb + (H-1) sh + Nq * 5 words; lse right after it does not overlap
+    assert call_m(lse=MB + 8 * 5 * 100, dtype=7) == ea.ATTN_EINVAL  # rejected for the dtype only
+
+
+@pytest.mark.parametrize("args", [
+    (0, MB, 4, 100), (Q, 0, 4, 100), (Q, MB, 0, 100), (Q, MB, 4, 0), (Q, MB + 4, 4, 100),
+    (Q, Q + 8, 4, 100),  # bits inside the mask bytes
+])
+def test_mask_pack_invalid_arguments(args):
+    assert ea.attn_mask_pack_ptr(*args, 0) == ea.ATTN_EINVAL
