@@ -13,6 +13,10 @@ CPU oracle timed on a bounded sample of the same workload on the host cores.
 With --pass bwd a step is one call of attn_bwd (D = rowsum(dO o O), then the
 dQ and dK/dV kernels) on the forward's o and lse, counted at 2.5 times the
 forward's flops (five N x N x d products instead of two).
+
+With --workload m1|m2|m3 a step is one call of attn_fwd_masked (unequal query and
+key lengths, a boolean mask packed once before timing), counted at 4*d flops per
+visible (query, key) pair.
 """
 from __future__ import annotations
 
@@ -151,6 +155,38 @@ def cpu_baseline_bwd(w, q, k, v, do, seconds: float):
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
 
+def visible_pairs(mw, mask) -> int:
+    """Visible (query, key) pairs of one head: the mask (if any) and the bottom-right
+    causal triangle (key j visible to query i iff j <= i + Nk - Nq)."""
+    import torch
+    vis = torch.ones((mw.Nq, mw.Nk), dtype=torch.bool) if mask is None else mask[0, 0].clone()
+    if mw.causal:
+        i = torch.arange(mw.Nq).view(-1, 1) + (mw.Nk - mw.Nq)
+        vis &= torch.arange(mw.Nk).view(1, -1) <= i
+    return int(vis.sum())
+
+
+def cpu_baseline_masked(mw, q, k, v, mask, pairs: int, seconds: float):
+    """The fp64 oracle's general-mask form on whole heads of the same workload, head
+    after head until `seconds` of wall time have been spent (at least one head)."""
+    import oracle
+    heads = [(b, h) for b in range(mw.B) for h in range(mw.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attn_masked(q[sl], k[sl], v[sl], mw.scale, mw.causal, mask)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * mw.d * pairs * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {mw.B * mw.H} heads, all {mw.Nq} query rows each "
+                      f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
+
+
 def copy_probe(nbytes: int, steps: int):
     """A plain device copy of known size (counter calibration run)."""
     import torch
@@ -168,7 +204,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1..c5 (default: c3, the headline)")
+    ap.add_argument("--workload", default="c3",
+                    help="c1..c5 (default: c3, the headline), or m1..m3 (masked / unequal lengths)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -198,10 +235,16 @@ def main():
 
     import torch
     import exact_attention_96_amd as ea
-    from exact_attention_96_amd.workloads import WORKLOADS, make_inputs, random_grad
+    from exact_attention_96_amd.workloads import MASKED_WORKLOADS, WORKLOADS, make_inputs, random_grad
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    if args.workload in MASKED_WORKLOADS:
+        if args.which != "fwd":
+            print("masked workloads time the forward only", file=sys.stderr)
+            sys.exit(2)
+        bench_masked(args, MASKED_WORKLOADS[args.workload])
         return
 
     w = WORKLOADS[args.workload]
@@ -286,6 +329,79 @@ def main():
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds) if bwd else
                                cpu_baseline(w, q, k, v, args.cpu_seconds))
+    print(json.dumps(out), flush=True)
+
+
+def time_steps(step, steps: int, warmup: int):
+    """Warmup, then `steps` timed calls: wall seconds and HIP-event ms per call on the
+    current stream (the stream the library is given)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def bench_masked(args, mw):
+    import torch
+    import exact_attention_96_amd as ea
+    print(f"[bench] workload {mw.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v, mask = mw.inputs()
+    dev = "cuda:0"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((mw.B, mw.H, mw.Nq), dtype=torch.float32, device=dev)
+    bits = None
+    pack_ms = None
+    if mask is not None:
+        md = mask.to(dev)
+        bits = ea.pack_mask(md)  # bits and tile summary, once, outside the timed region
+        torch.cuda.synchronize()
+        _, pk = time_steps(lambda: ea.pack_mask(md), 10, 2)
+        pack_ms = sum(pk) / len(pk)
+
+    def step():
+        ea.attn_fwd_masked(qd, kd, vd, mask_bits=bits, causal=mw.causal, scale=mw.scale, out=o, lse=lse)
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    wall, kernel_ms = time_steps(step, args.steps, args.warmup)
+    pairs = visible_pairs(mw, mask)
+    flops = 4.0 * mw.d * pairs * mw.B * mw.H
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / avg_kernel_s / 1e12
+    peak = PEAK_MFMA_BF16_TFLOPS
+    out = {
+        "metric": "attention fwd TFLOP/s (masked / unequal lengths) and % of MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": mw.dtype,
+        "data": "synthetic (seeded randn inputs and mask patterns, see exact_attention_96_amd/workloads.py)",
+        "config": {"workload": mw.name, "B": mw.B, "H": mw.H, "Nq": mw.Nq, "Nk": mw.Nk, "d": mw.d,
+                   "causal": mw.causal, "mask": mw.mask_kind, "mask_w": mw.mask_w, "scale": mw.scale,
+                   "visible_pairs_per_head": pairs},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes": mw.io_bytes + (0 if bits is None else bits.bits.numel() * 8),
+                     "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
+                     "kernel_source_sha": kernel_source_hash()},
+        "mask_pack_ms": None if pack_ms is None else round(pack_ms, 4),
+    }
+    if args.cpu_seconds > 0 and args.cpu_heads != 0:
+        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_masked(mw, q, k, v, mask, pairs, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

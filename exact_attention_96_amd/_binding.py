@@ -44,10 +44,10 @@ def lib() -> ctypes.CDLL:
                                ci, ci, vp]
         L.attn_bwd.restype = ci
         ll = ctypes.c_longlong
-        L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, ll, ll, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float,
-                                      ci, ci, vp]
+        L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, ll, ll, vp, vp, ci, ci, ci, ci, ci,
+                                      ctypes.c_float, ci, ci, vp]
         L.attn_fwd_masked.restype = ci
-        L.attn_mask_pack.argtypes = [vp, vp, ll, ci, vp]
+        L.attn_mask_pack.argtypes = [vp, vp, vp, ll, ci, ci, vp]
         L.attn_mask_pack.restype = ci
         L.attn_strerror.argtypes = [ci]
         L.attn_strerror.restype = ctypes.c_char_p
@@ -72,17 +72,20 @@ def attn_fwd_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: in
                               causal, dtype, stream))
 
 
-def attn_fwd_masked_ptr(q: int, k: int, v: int, mask_bits: int | None, mask_stride_b: int,
-                        mask_stride_h: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int, d: int,
-                        scale: float, causal: int, dtype: int, stream: int) -> int:
-    """Raw call with integer device addresses (mask_bits None or 0: no mask)."""
-    return int(lib().attn_fwd_masked(q, k, v, mask_bits or None, mask_stride_b, mask_stride_h, o, lse,
-                                     B, H, Nq, Nk, d, ctypes.c_float(scale), causal, dtype, stream))
+def attn_fwd_masked_ptr(q: int, k: int, v: int, mask_bits: int | None, mask_tiles: int | None,
+                        mask_stride_b: int, mask_stride_h: int, o: int, lse: int, B: int, H: int,
+                        Nq: int, Nk: int, d: int, scale: float, causal: int, dtype: int,
+                        stream: int) -> int:
+    """Raw call with integer device addresses (None or 0: no mask / no tile summary)."""
+    return int(lib().attn_fwd_masked(q, k, v, mask_bits or None, mask_tiles or None, mask_stride_b,
+                                     mask_stride_h, o, lse, B, H, Nq, Nk, d, ctypes.c_float(scale),
+                                     causal, dtype, stream))
 
 
-def attn_mask_pack_ptr(mask: int, bits: int, rows: int, Nk: int, stream: int) -> int:
-    """Raw call with integer device addresses; returns the status code."""
-    return int(lib().attn_mask_pack(mask, bits, rows, Nk, stream))
+def attn_mask_pack_ptr(mask: int, bits: int, tiles: int | None, heads: int, Nq: int, Nk: int,
+                       stream: int) -> int:
+    """Raw call with integer device addresses (tiles None or 0: no summary)."""
+    return int(lib().attn_mask_pack(mask, bits, tiles or None, heads, Nq, Nk, stream))
 
 
 def attn_bwd_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
@@ -146,10 +149,22 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     return out, lse
 
 
-def pack_mask(mask):
+class PackedMask(tuple):
+    """(bits, tiles) of a packed mask: bits int64 [Bm, Hm, Nq, ceil(Nk / 64)], bit j % 64
+    of word j / 64 = key j visible; tiles int64 [Bm, Hm, ceil(Nq / 256), ceil(Nk / 4096)]
+    (or None), the per-256-row-tile summary of which 64-key units any row sees."""
+
+    def __new__(cls, bits, tiles):
+        return super().__new__(cls, (bits, tiles))
+
+    bits = property(lambda self: self[0])
+    tiles = property(lambda self: self[1])
+
+
+def pack_mask(mask, tiles: bool = True) -> PackedMask:
     """Packs a boolean mask [Bm, Hm, Nq, Nk] (torch.bool or uint8, contiguous, on a HIP
-    device; nonzero = key visible) into the bit format of attn_fwd_masked: an int64
-    tensor [Bm, Hm, Nq, ceil(Nk / 64)] whose bit j % 64 of word j / 64 is key j.  The
+    device; nonzero = key visible) into the format of attn_fwd_masked, with the tile
+    summary that lets the kernel skip empty key units (tiles=False: bits only).  The
     packing runs on the GPU (attn_mask_pack) on torch's current stream."""
     import torch
     if not isinstance(mask, torch.Tensor):
@@ -161,14 +176,18 @@ def pack_mask(mask):
     if mask.dim() != 4 or not mask.is_contiguous():
         raise ValueError("mask must be a contiguous [Bm, Hm, Nq, Nk] tensor")
     Bm, Hm, Nq, Nk = mask.shape
-    rows = Bm * Hm * Nq
-    bits = torch.empty((Bm, Hm, Nq, (Nk + 63) // 64), dtype=torch.int64, device=mask.device)
+    W = (Nk + 63) // 64
+    bits = torch.empty((Bm, Hm, Nq, W), dtype=torch.int64, device=mask.device)
+    tl = None
+    if tiles:
+        tl = torch.empty((Bm, Hm, (Nq + 255) // 256, (W + 63) // 64), dtype=torch.int64, device=mask.device)
     with torch.cuda.device(mask.device):
         stream = torch.cuda.current_stream(mask.device).cuda_stream
-        st = attn_mask_pack_ptr(mask.data_ptr(), bits.data_ptr(), rows, Nk, stream)
+        st = attn_mask_pack_ptr(mask.data_ptr(), bits.data_ptr(), None if tl is None else tl.data_ptr(),
+                                Bm * Hm, Nq, Nk, stream)
     if st != ATTN_OK:
         raise AttnError(st, strerror(st), "attn_mask_pack")
-    return bits
+    return PackedMask(bits, tl)
 
 
 def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | None = None,
@@ -178,7 +197,8 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
     q: [B, H, Nq, d]; k, v: [B, H, Nk, d]; one HIP device, one dtype, contiguous.
     mask: None, or a boolean mask [Bm, Hm, Nq, Nk] (Bm in {1, B}, Hm in {1, H}; true =
     visible), packed on the GPU first; or mask_bits: an already packed mask (see
-    pack_mask).  causal: keys j > i + Nk - Nq are hidden as well.  Returns (o, lse):
+    pack_mask; a PackedMask, or a bare bits tensor for no unit skipping).  causal:
+    keys j > i + Nk - Nq are hidden as well.  Returns (o, lse):
     o like q, lse float32 [B, H, Nq]; a row that sees no key gets o = 0, lse = -inf.
     """
     import torch
@@ -209,7 +229,11 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
             raise ValueError("mask must be a tensor on q's device")
         mask_bits = pack_mask(mask)
     sb = sh = 0
-    mptr = None
+    mptr = tptr = None
+    if isinstance(mask_bits, PackedMask):
+        mask_bits, tiles = mask_bits
+    else:
+        tiles = None
     if mask_bits is not None:
         W = (Nk + 63) // 64
         if not isinstance(mask_bits, torch.Tensor) or mask_bits.dtype != torch.int64 \
@@ -219,9 +243,15 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
         if Bm not in (1, B) or Hm not in (1, H) or tuple(mask_bits.shape[2:]) != (Nq, W):
             raise ValueError(f"mask of shape {tuple(mask_bits.shape)} does not match "
                              f"[{B} or 1, {H} or 1, {Nq}, {W}]")
-        sb = 0 if Bm == 1 else Hm * Nq * W
-        sh = 0 if Hm == 1 else Nq * W
+        sb = 0 if Bm == 1 else Hm
+        sh = 0 if Hm == 1 else 1
         mptr = mask_bits.data_ptr()
+        if tiles is not None:
+            if not isinstance(tiles, torch.Tensor) or tiles.dtype != torch.int64 or not tiles.is_contiguous() \
+                    or tiles.device != q.device \
+                    or tuple(tiles.shape) != (Bm, Hm, (Nq + 255) // 256, (W + 63) // 64):
+                raise ValueError("mask tiles do not match the mask bits")
+            tptr = tiles.data_ptr()
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -233,7 +263,7 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = attn_fwd_masked_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, sb, sh, out.data_ptr(),
+        st = attn_fwd_masked_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, tptr, sb, sh, out.data_ptr(),
                                  lse.data_ptr(), B, H, Nq, Nk, d, float(scale), int(bool(causal)), code,
                                  stream)
     if st != ATTN_OK:

@@ -110,6 +110,31 @@ __global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t *mask
     }
 }
 
+// Tile summary of packed bits [heads, Nq, W]: one wave per (head, query tile t, word
+// wi of the summary row), lane = unit wi * 64 + lane; the lane ORs the unit's word
+// over the tile's rows and the wave's ballot is the summary word.
+__global__ __launch_bounds__(256) void attn_mask_tiles_kernel(const uint64_t *bits, uint64_t *tiles, long long words,
+                                                              int Nq, int W, int nt, int tw) {
+    const int lane = threadIdx.x & 63;
+    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long n_waves = (long long)gridDim.x * 4;
+    for (long long i = wave; i < words; i += n_waves) {
+        const long long ht = i / tw;  // head * nt + t
+        const int wi = (int)(i - ht * tw);
+        const long long head = ht / nt;
+        const int t = (int)(ht - head * nt);
+        const int u = wi * 64 + lane;
+        uint64_t any = 0;
+        if (u < W) {
+            const int r0 = t * attn::kMaskTileRows, r1 = min(r0 + attn::kMaskTileRows, Nq);
+            const uint64_t *col = bits + (head * Nq + r0) * (long long)W + u;
+            for (int r = r0; r < r1; ++r, col += W) any |= *col;
+        }
+        const uint64_t word = __builtin_amdgcn_ballot_w64(any != 0);
+        if (lane == 0) tiles[i] = word;
+    }
+}
+
 // Backward: D_i = dO_i . O_i, then dQ and dK/dV (independent of each other).
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs &a, int bh, hipStream_t stream) {
@@ -146,9 +171,9 @@ hipError_t bwd_causal(const BwdArgs &a, int bh, int causal, int dtype, hipStream
 }
 
 // Checks and launch shared by attn_fwd and attn_fwd_masked (mask may be NULL).
-int fwd_core(const void *q, const void *k, const void *v, const void *mask, long long msb, long long msh, void *o,
-             float *lse, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
-             hipStream_t stream) {
+int fwd_core(const void *q, const void *k, const void *v, const void *mask, const void *tiles, long long msb,
+             long long msh, void *o, float *lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+             int dtype, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_EINVAL;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
@@ -162,22 +187,30 @@ int fwd_core(const void *q, const void *k, const void *v, const void *mask, long
     const uint64_t qb = rows_q * (uint64_t)d * elt, kb = rows_k * (uint64_t)d * elt;
     const uint64_t lbytes = rows_q * 4;
     const uint64_t mw = ((uint64_t)Nk + 63) / 64;  // mask words per row
-    uint64_t mbytes = 0;
+    const uint64_t nt = ((uint64_t)Nq + attn::kMaskTileRows - 1) / attn::kMaskTileRows;  // summary tiles per head
+    const uint64_t tw = (mw + 63) / 64;                                                 // summary words per tile
+    uint64_t mbytes = 0, tbytes = 0;
+    if (tiles && !mask) return ATTN_EINVAL;
     if (mask) {
-        if (!aligned(mask, 8) || msb < 0 || msh < 0) return ATTN_EINVAL;
-        // one past the last word read: (B-1) sb + (H-1) sh + Nq mw (checked in 64 bits)
-        if ((uint64_t)msb > (1ull << 40) || (uint64_t)msh > (1ull << 40)) return ATTN_EUNSUPPORTED;
-        mbytes = ((uint64_t)(B - 1) * (uint64_t)msb + (uint64_t)(H - 1) * (uint64_t)msh + (uint64_t)Nq * mw) * 8;
+        if (!aligned(mask, 8) || (tiles && !aligned(tiles, 8)) || msb < 0 || msh < 0) return ATTN_EINVAL;
+        if ((uint64_t)msb > (1ull << 31) || (uint64_t)msh > (1ull << 31)) return ATTN_EUNSUPPORTED;
+        // mask heads read: 0 .. (B-1) sb + (H-1) sh (checked in 64 bits)
+        const uint64_t heads = (uint64_t)(B - 1) * (uint64_t)msb + (uint64_t)(H - 1) * (uint64_t)msh + 1;
+        mbytes = heads * (uint64_t)Nq * mw * 8;
+        tbytes = tiles ? heads * nt * tw * 8 : 0;
     }
     if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) || overlaps(lse, lbytes, q, qb) ||
         overlaps(lse, lbytes, k, kb) || overlaps(lse, lbytes, v, kb) || overlaps(lse, lbytes, o, qb))
         return ATTN_EINVAL;
     if (mask && (overlaps(o, qb, mask, mbytes) || overlaps(lse, lbytes, mask, mbytes))) return ATTN_EINVAL;
+    if (tiles && (overlaps(o, qb, tiles, tbytes) || overlaps(lse, lbytes, tiles, tbytes))) return ATTN_EINVAL;
     if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
     // the smallest query tile is 32 rows; the 1-D grid holds at most INT32_MAX workgroups
     if ((uint64_t)B * (uint64_t)H * (((uint64_t)Nq + 31) / 32) > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
     // a head's mask rows are addressed with 32-bit byte offsets
     if (mask && (uint64_t)Nq * mw * 8 > (uint64_t)UINT32_MAX) return ATTN_EUNSUPPORTED;
+    // the unit list of a query tile lives in LDS
+    if (tiles && mw > (uint64_t)attn::MfmaFwd<__bf16, 128, false, attn::kFwdBits>::LIST_CAP) return ATTN_EUNSUPPORTED;
 
     FwdArgs a;
     a.q = q;
@@ -196,6 +229,9 @@ int fwd_core(const void *q, const void *k, const void *v, const void *mask, long
     a.mask_sh = msh;
     a.mask_w = (int)mw;
     a.H = H;
+    a.tiles = static_cast<const uint64_t *>(tiles);
+    a.tiles_w = (int)tw;
+    a.tiles_nt = (int)nt;
     const int bh = B * H;
     const hipError_t err = d == 64 ? dispatch_mode<64>(a, bh, causal, dtype, stream)
                                    : dispatch_mode<128>(a, bh, causal, dtype, stream);
@@ -206,28 +242,38 @@ int fwd_core(const void *q, const void *k, const void *v, const void *mask, long
 
 extern "C" ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                                  int N, int d, float scale, int causal, int dtype, hipStream_t stream) {
-    return fwd_core(q, k, v, nullptr, 0, 0, o, lse, B, H, N, N, d, scale, causal, dtype, stream);
+    return fwd_core(q, k, v, nullptr, nullptr, 0, 0, o, lse, B, H, N, N, d, scale, causal, dtype, stream);
 }
 
 extern "C" ATTN_API int attn_fwd_masked(const void *q, const void *k, const void *v, const void *mask_bits,
-                                        long long mask_stride_b, long long mask_stride_h, void *o, float *lse, int B,
-                                        int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
-                                        hipStream_t stream) {
-    return fwd_core(q, k, v, mask_bits, mask_stride_b, mask_stride_h, o, lse, B, H, Nq, Nk, d, scale, causal, dtype,
-                    stream);
+                                        const void *mask_tiles, long long mask_stride_b, long long mask_stride_h,
+                                        void *o, float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+                                        int causal, int dtype, hipStream_t stream) {
+    return fwd_core(q, k, v, mask_bits, mask_tiles, mask_stride_b, mask_stride_h, o, lse, B, H, Nq, Nk, d, scale,
+                    causal, dtype, stream);
 }
 
-extern "C" ATTN_API int attn_mask_pack(const void *mask, void *bits, long long rows, int Nk, hipStream_t stream) {
-    if (!mask || !bits || rows < 1 || Nk < 1) return ATTN_EINVAL;
-    if (!aligned(bits, 8)) return ATTN_EINVAL;
+extern "C" ATTN_API int attn_mask_pack(const void *mask, void *bits, void *tiles, long long heads, int Nq, int Nk,
+                                       hipStream_t stream) {
+    if (!mask || !bits || heads < 1 || Nq < 1 || Nk < 1) return ATTN_EINVAL;
+    if (!aligned(bits, 8) || (tiles && !aligned(tiles, 8))) return ATTN_EINVAL;
     const uint64_t w = ((uint64_t)Nk + 63) / 64;
-    if ((uint64_t)rows > (1ull << 40) / w) return ATTN_EUNSUPPORTED;
-    const uint64_t words = (uint64_t)rows * w;
-    if (overlaps(bits, words * 8, mask, (uint64_t)rows * (uint64_t)Nk)) return ATTN_EINVAL;
+    const uint64_t nt = ((uint64_t)Nq + attn::kMaskTileRows - 1) / attn::kMaskTileRows, tw = (w + 63) / 64;
+    if ((uint64_t)heads > (1ull << 40) / ((uint64_t)Nq * w)) return ATTN_EUNSUPPORTED;
+    const uint64_t rows = (uint64_t)heads * (uint64_t)Nq;
+    const uint64_t words = rows * w, twords = (uint64_t)heads * nt * tw;
+    if (overlaps(bits, words * 8, mask, rows * (uint64_t)Nk)) return ATTN_EINVAL;
+    if (tiles && (overlaps(tiles, twords * 8, mask, rows * (uint64_t)Nk) || overlaps(tiles, twords * 8, bits, words * 8)))
+        return ATTN_EINVAL;
     const uint64_t blocks = (words + 3) / 4;
-    const int grid = (int)(blocks < 65536 ? blocks : 65536);
-    const hipError_t e = launch(&attn_mask_pack_kernel, grid, 256, 0, stream, static_cast<const uint8_t *>(mask),
-                                static_cast<uint64_t *>(bits), (long long)words, Nk, (int)w);
+    hipError_t e = launch(&attn_mask_pack_kernel, (int)(blocks < 65536 ? blocks : 65536), 256, 0, stream,
+                          static_cast<const uint8_t *>(mask), static_cast<uint64_t *>(bits), (long long)words, Nk,
+                          (int)w);
+    if (e != hipSuccess || !tiles) return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+    const uint64_t tblocks = (twords + 3) / 4;
+    e = launch(&attn_mask_tiles_kernel, (int)(tblocks < 65536 ? tblocks : 65536), 256, 0, stream,
+               static_cast<const uint64_t *>(bits), static_cast<uint64_t *>(tiles), (long long)twords, Nq, (int)w,
+               (int)nt, (int)tw);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

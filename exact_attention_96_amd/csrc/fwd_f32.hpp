@@ -53,8 +53,8 @@ struct F32Fwd {
         const uint64_t *mrow = nullptr;
         if (MASK) {
             const int b = bh / a.H, hh = bh - b * a.H;
-            mrow = a.mask + (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh +
-                   (size_t)min(qrow, Nq - 1) * (size_t)a.mask_w;
+            const size_t mhead = (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh;
+            mrow = a.mask + (mhead * (size_t)Nq + (size_t)min(qrow, Nq - 1)) * (size_t)a.mask_w;
         }
         // causal: the workgroup's last row sees keys up to its index + off
         const int n_kv_all = (Nk + BK - 1) / BK;

@@ -69,13 +69,25 @@ struct FwdArgs {
     int total;       // B * H * n_qtiles
     float c;         // scale * log2(e)
     // Optional bit mask (kernels instantiated with MASK only): bit j % 64 of word
-    // j / 64 of row i is 1 iff key j is visible to query i.  Head (b, h) starts at
-    // word b * mask_sb + h * mask_sh; rows are mask_w = ceil(Nk / 64) words apart.
+    // j / 64 of row i is 1 iff key j is visible to query i.  Head (b, h) uses mask
+    // head m = b * mask_sb + h * mask_sh, which starts at word m * Nq * mask_w; rows
+    // are mask_w = ceil(Nk / 64) words apart.
     const uint64_t *mask;
     long long mask_sb, mask_sh;
     int mask_w;
     int H;
+    // Optional tile summary of the mask (matrix-core kernels only): for mask head m
+    // and query tile t of kMaskTileRows rows, tiles_w words starting at word
+    // (m * tiles_nt + t) * tiles_w; bit u % 64 of word u / 64 is 1 iff some row of
+    // the tile sees a key of unit u (keys 64 u .. 64 u + 63).  NULL: no summary.
+    const uint64_t *tiles;
+    int tiles_w, tiles_nt;
 };
+
+// Query rows per tile of the mask summary (the matrix-core kernel's query tile).
+constexpr int kMaskTileRows = 256;
+// Keys per unit of the mask summary.
+constexpr int kMaskUnitKeys = 64;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -194,7 +206,10 @@ struct MfmaFwd {
     static constexpr int V_BASE = STAGES * UNIT_B;   // V ring follows the K ring
     static constexpr int MUNIT_B = BR * 8;           // mask bits of one unit: a 64-bit word per row
     static constexpr int M_BASE = 2 * STAGES * UNIT_B;  // mask ring follows the V ring
-    static constexpr int LDS_B = M_BASE + (MASK ? STAGES * MUNIT_B : 0);
+    static constexpr int LIST_BASE = M_BASE + STAGES * MUNIT_B;  // unit list (MASK) follows the mask ring
+    static constexpr int LIST_CAP = 4096;            // units of the list: Nk <= 262144 with a summary
+    static constexpr int LDS_B = MASK ? LIST_BASE + 4 * LIST_CAP : M_BASE;
+    static_assert(!MASK || (BR == kMaskTileRows && BU == kMaskUnitKeys), "summary tiles are query tiles and units");
     static constexpr int LOADS = BU * CH / 64 / NW;  // 16-byte-per-lane DMA loads per wave, unit and tensor
     static constexpr int KVLOADS = 2 * LOADS;        // K and V loads per wave in one load group
     static constexpr int GROUP = KVLOADS + (MASK ? 1 : 0);  // plus one 4-byte mask load per wave
@@ -524,9 +539,11 @@ struct MfmaFwd {
         // workgroup row (64 w + lane) / 2, stored densely (8 bytes per row) in LDS.  The
         // lane's source offset is recomputed per load (registers are scarce in the loop).
         const uint64_t *Mh = nullptr;
+        size_t mhead = 0;  // mask head of (b, h)
         if (MASK) {
             const int b = bh / a.H, hh = bh - b * a.H;
-            Mh = a.mask + (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh;
+            mhead = (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh;
+            Mh = a.mask + mhead * (size_t)Nq * (size_t)a.mask_w;
             S.mrow = lds0 + M_BASE + (uint32_t)(S.r0 - qt * BR + l32) * 8u;
         }
         auto mask_src = [&]() -> uint32_t {
@@ -539,8 +556,42 @@ struct MfmaFwd {
         // unit so that every load is in bounds; waves without keys only pass barriers.
         auto units_to = [&](int last_key) { return last_key < 0 ? 0 : last_key / BU + 1; };
         const int n_units = (Nk + BU - 1) / BU;
-        const int nu_wg = CAUSAL ? max(1, min(n_units, units_to(min(qt * BR + BR, Nq) - 1 + off))) : n_units;
-        const int nu = S.r0 >= Nq ? 0 : (CAUSAL ? min(n_units, units_to(min(S.r0 + 31, Nq - 1) + off)) : n_units);
+        int nu_wg = CAUSAL ? max(1, min(n_units, units_to(min(qt * BR + BR, Nq) - 1 + off))) : n_units;
+        int nu = S.r0 >= Nq ? 0 : (CAUSAL ? min(n_units, units_to(min(S.r0 + 31, Nq - 1) + off)) : n_units);
+        // Unit schedule (MASK with a tile summary): the workgroup visits only the units in
+        // which some row of its query tile sees a key, in increasing order; position p
+        // of the loop below is unit list[p] (LDS).  nu_wg and nu become position counts
+        // (this wave: the listed units it needs).  Without a summary position p is unit p.
+        // A tile that sees no key at all still loads unit 0 (list[0] = 0) and computes
+        // nothing, so that every load is in bounds.
+        const bool use_list = MASK && a.tiles != nullptr;
+        if (use_list) {
+            const uint64_t *tw = a.tiles + (mhead * (size_t)a.tiles_nt + (size_t)qt) * (size_t)a.tiles_w;
+            int cnt = 0, cnt_w = 0;
+            for (int wi = 0; wi * 64 < nu_wg; ++wi) {
+                uint64_t bits = tw[wi];
+                const int lim_wg = nu_wg - wi * 64, lim_w = nu - wi * 64;
+                if (lim_wg < 64) bits &= (1ull << lim_wg) - 1ull;
+                const uint64_t bits_w = lim_w <= 0 ? 0ull : (lim_w >= 64 ? bits : bits & ((1ull << lim_w) - 1ull));
+                if (w == 0 && ((bits >> lane) & 1ull)) {
+                    const int pos = cnt + __builtin_popcountll(bits & ((1ull << lane) - 1ull));
+                    *(__attribute__((address_space(3))) int *)(uintptr_t)(lds0 + LIST_BASE + 4 * pos) = wi * 64 + lane;
+                }
+                cnt += __builtin_popcountll(bits);
+                cnt_w += __builtin_popcountll(bits_w);
+            }
+            if (w == 0 && lane == 0 && cnt == 0) *(__attribute__((address_space(3))) int *)(uintptr_t)(lds0 + LIST_BASE) = 0;
+            nu_wg = max(cnt, 1);
+            nu = cnt_w;
+            __syncthreads();
+        }
+        // unit at loop position p (wave-uniform)
+        auto unit_at = [&](int p) -> int {
+            if (MASK && use_list)
+                return __builtin_amdgcn_readfirstlane(
+                    *(const __attribute__((address_space(3))) int *)(uintptr_t)(lds0 + LIST_BASE + 4 * p));
+            return p;
+        };
         // The first nm units are visible to every row of the wave (no caller mask, keys
         // below the first row's diagonal and the sequence end) and take the unmasked
         // softmax; the rest of the wave's units (at least the last one) are masked.
@@ -569,22 +620,29 @@ struct MfmaFwd {
         // into stages nobody reads any more, so that every group is GROUP loads and
         // the waits below are constant counts.  issue_part(i, j) issues load j of the
         // group (K loads first, then V loads, then the mask load).
-        auto issue_part = [&](int i, int j) {
+        // The units of group i are looked up once per step (un = units(i)), before the
+        // matrix phase that issues the group.
+        struct Units {
+            int k, v;  // unit of the K load and of the V (and mask) loads
+        };
+        auto units = [&](int i) { return Units{unit_at(min(i, nu_wg - 1)), unit_at(min(i - 1, nu_wg - 1))}; };
+        auto issue_part = [&](const Units &un, int i, int j) {
             if (j < LOADS)
-                load_one(Kh, (i % STAGES) * UNIT_B, kld[j], min(i, nu_wg - 1), j);
+                load_one(Kh, (i % STAGES) * UNIT_B, kld[j], un.k, j);
             else if (j < KVLOADS)
-                load_one(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld[j - LOADS], min(i - 1, nu_wg - 1), j - LOADS);
+                load_one(Vh, V_BASE + ((i - 1) % STAGES) * UNIT_B, vld[j - LOADS], un.v, j - LOADS);
             else
-                dma_to_lds4(Mh + min(i - 1, nu_wg - 1), mask_src(), lds0 + M_BASE + ((i - 1) % STAGES) * MUNIT_B + w * 256);
+                dma_to_lds4(Mh + un.v, mask_src(), lds0 + M_BASE + ((i - 1) % STAGES) * MUNIT_B + w * 256);
         };
         // the mask load of a group goes first in its step, the K/V loads are spread
         // over the P V MFMAs by gemm
-        auto issue_mask = [&](int i) {
-            if (MASK) issue_part(i, KVLOADS);
+        auto issue_mask = [&](const Units &un, int i) {
+            if (MASK) issue_part(un, i, KVLOADS);
         };
         auto issue = [&](int i) {
+            const Units un = units(i);
 #pragma unroll
-            for (int j = 0; j < GROUP; ++j) issue_part(i, j);
+            for (int j = 0; j < GROUP; ++j) issue_part(un, i, j);
         };
 
         // Barriers wait for this wave's DMA.  Data of load group i is read from the
@@ -628,8 +686,9 @@ struct MfmaFwd {
         };
         auto plain_step = [&](auto st, int u) {
             constexpr int ST = decltype(st)::value;  // u mod STAGES
-            issue_mask(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+            const Units un = units(u + STAGES - 1);
+            issue_mask(un, u + STAGES - 1);
+            gemm(S, s, pk, kf, ((ST + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((ST + 1) % STAGES) * UNIT_B);
             soft<false, false>(S, s, pk, u * BU);
@@ -638,7 +697,7 @@ struct MfmaFwd {
         };
 
         // prologue: group 0 is K of unit 0 only (V stage STAGES - 1 holds zeros)
-        load_unit(Kh, 0, kld, 0);
+        load_unit(Kh, 0, kld, unit_at(0));
         for (int i = 1; i < STAGES - 1; ++i) issue(i);
         barrier_mid();
         kload(S, kf, 0);
@@ -647,8 +706,9 @@ struct MfmaFwd {
         if (!MASK && nm > 0) {
             // unit 0 (plain, first of the tile), then the plain units up to nm - 1,
             // unrolled by four from unit 1 so that the ring stage is an immediate
-            issue_mask(STAGES - 1);
-            gemm(S, s, pk, kf, (STAGES - 1) * UNIT_B, [&](int j) { issue_part(STAGES - 1, j); });
+            const Units un = units(STAGES - 1);
+            issue_mask(un, STAGES - 1);
+            gemm(S, s, pk, kf, (STAGES - 1) * UNIT_B, [&](int j) { issue_part(un, STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, 1 * UNIT_B);
             soft<false, true>(S, s, pk, 0);
@@ -662,8 +722,9 @@ struct MfmaFwd {
                 plain_step(std::integral_constant<int, 0>(), u + 3);
             }
             for (; u < nm; ++u) {  // remaining plain steps, ring stage from u
-                issue_mask(u + STAGES - 1);
-                gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+                const Units un = units(u + STAGES - 1);
+                issue_mask(un, u + STAGES - 1);
+                gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
                 barrier_mid();
                 kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
                 soft<false, false>(S, s, pk, u * BU);
@@ -672,12 +733,13 @@ struct MfmaFwd {
             }
         }
         auto masked_step = [&]() {
-            issue_mask(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+            const Units un = units(u + STAGES - 1);
+            issue_mask(un, u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
             barrier_mid();
             kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
             if (MODE != kFwdPlain)  // a reference still at -inf takes the row max
-                soft<true, false>(S, s, pk, u * BU, (u % STAGES) * MUNIT_B);
+                soft<true, false>(S, s, pk, unit_at(u) * BU, (u % STAGES) * MUNIT_B);
             else if (u == 0)
                 soft<true, true>(S, s, pk, u * BU);
             else
@@ -695,8 +757,9 @@ struct MfmaFwd {
             ++u;
         }
         if (nu > 0) {  // step nu: P V of the last unit (u = nu)
-            issue_mask(u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(u + STAGES - 1, j); });
+            const Units un = units(u + STAGES - 1);
+            issue_mask(un, u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
             barrier_mid();
             barrier_end();
             ++u;

@@ -162,3 +162,56 @@ def random_mask(kind: str, Bm: int, Hm: int, Nq: int, Nk: int, seed: int, **kw) 
         rows = torch.rand((Bm, Hm, Nq, 1), generator=g) < 0.1
         return (m & ~rows).contiguous()
     raise ValueError(f"unknown mask kind {kind!r}")
+
+
+@dataclass(frozen=True)
+class MaskedWorkload:
+    """A workload of attn_fwd_masked: q [B, H, Nq, d], k and v [B, H, Nk, d] drawn by
+    random_qkv_lens, and a mask [1, 1, Nq, Nk] shared by every head drawn by
+    random_mask(mask_kind, ...) (None: no mask)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    mask_kind: str | None = None
+    mask_w: int = 0          # window length for mask_kind "window"
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def elt(self) -> int:
+        return torch.tensor([], dtype=DTYPES[self.dtype]).element_size()
+
+    @property
+    def io_bytes(self) -> int:
+        """Read Q, K, V once, write O and lse once (the packed mask is counted apart)."""
+        return (2 * self.B * self.H * (self.Nq + self.Nk) * self.d * self.elt
+                + 4 * self.B * self.H * self.Nq)
+
+    def inputs(self):
+        q, k, v = random_qkv_lens(self.B, self.H, self.Nq, self.Nk, self.d, self.dtype, self.seed)
+        mask = None
+        if self.mask_kind is not None:
+            mask = random_mask(self.mask_kind, 1, 1, self.Nq, self.Nk, self.seed + 1, w=self.mask_w)
+        return q, k, v, mask
+
+
+# Masked and unequal-length workloads at the headline head shape (B=2, H=32, d=128, bf16).
+MASKED_WORKLOADS = {
+    # the causal mask materialised as a boolean lower triangle (the math backend's form)
+    "m1": MaskedWorkload("m1_bf16_tril_mask_b2h32n8192d128", 2, 32, 8192, 8192, 128, "bf16", False,
+                         mask_kind="window", mask_w=8192, seed=101),
+    # a causal sliding window of 1024 keys given as a mask
+    "m2": MaskedWorkload("m2_bf16_window1024_b2h32n8192d128", 2, 32, 8192, 8192, 128, "bf16", True,
+                         mask_kind="window", mask_w=1024, seed=102),
+    # chunked prefill: the last 2048 of 8192 positions, causal from the bottom-right corner
+    "m3": MaskedWorkload("m3_bf16_causal_nq2048_nk8192_b2h32d128", 2, 32, 2048, 8192, 128, "bf16",
+                         True, seed=103),
+}

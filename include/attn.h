@@ -114,12 +114,19 @@ ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, floa
  *   q        device pointer, [B, H, Nq, d] contiguous of `dtype`; read only.
  *   k, v     device pointers, [B, H, Nk, d] contiguous of `dtype`; read only.
  *   mask_bits  NULL (no mask) or a device pointer to 64-bit words, 8-byte
- *            aligned, as written by attn_mask_pack: the mask of head (b, h) is
- *            Nq rows of ceil(Nk / 64) words starting at word
- *            b * mask_stride_b + h * mask_stride_h; bit j % 64 of word j / 64 of
- *            row i is 1 iff key j is visible to query i.  A stride of 0 shares
- *            one mask across that axis.  Read only.
- *   mask_stride_b, mask_stride_h  word strides, >= 0 (ignored without a mask).
+ *            aligned, as written by attn_mask_pack: mask head m is Nq rows of
+ *            W = ceil(Nk / 64) words starting at word m * Nq * W; bit j % 64 of
+ *            word j / 64 of row i is 1 iff key j is visible to query i.  Head
+ *            (b, h) uses mask head m = b * mask_stride_b + h * mask_stride_h.
+ *            Read only.
+ *   mask_tiles NULL, or (with mask_bits) the tile summary attn_mask_pack wrote for
+ *            the same mask heads: the bf16/fp16 kernels then skip, per 256-row
+ *            query tile, the 64-key units no row of the tile can see (W <= 4096
+ *            keeps the unit list on chip).  It must describe mask_bits exactly:
+ *            a unit marked empty is never read.  fp32 ignores it.  Read only.
+ *   mask_stride_b, mask_stride_h  mask-head strides, 0 .. 2^31 (0 shares one
+ *            mask across that axis; [B, H] masks use H and 1); ignored without
+ *            a mask.
  *   o        device pointer, [B, H, Nq, d] contiguous of `dtype`; written.
  *   lse      device pointer, [B, H, Nq] contiguous fp32; written.
  *   B, H, Nq, Nk  batch, heads, query and key lengths, each >= 1.
@@ -130,38 +137,44 @@ ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, floa
  * lse must not overlap q, k, v, the mask words read or each other.
  *
  * Errors are returned synchronously and nothing is launched on error:
- *   ATTN_EINVAL       as attn_fwd (with Nq, Nk in place of N); a mask not
- *                     8-byte aligned or a negative stride; o or lse overlapping
- *                     the mask words.
- *   ATTN_EUNSUPPORTED as attn_fwd; a head's mask larger than 4 GiB; a stride
- *                     above 2^40.
+ *   ATTN_EINVAL       as attn_fwd (with Nq, Nk in place of N); mask_tiles
+ *                     without mask_bits; mask words not 8-byte aligned; a
+ *                     negative stride; o or lse overlapping the mask words.
+ *   ATTN_EUNSUPPORTED as attn_fwd; a mask head larger than 4 GiB; a stride
+ *                     above 2^31; mask_tiles with W > 4096.
  *   ATTN_EHIP         as attn_fwd.
  */
 ATTN_API int attn_fwd_masked(const void *q, const void *k, const void *v, const void *mask_bits,
-                             long long mask_stride_b, long long mask_stride_h, void *o, float *lse,
-                             int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                             int dtype, hipStream_t stream);
+                             const void *mask_tiles, long long mask_stride_b,
+                             long long mask_stride_h, void *o, float *lse, int B, int H, int Nq,
+                             int Nk, int d, float scale, int causal, int dtype,
+                             hipStream_t stream);
 
 /*
  * attn_mask_pack — packs a boolean mask into the bit format of attn_fwd_masked.
  *
  * Arguments
- *   mask     device pointer, [rows, Nk] contiguous bytes; nonzero = visible
+ *   mask     device pointer, [heads, Nq, Nk] contiguous bytes; nonzero = visible
  *            ("PyTorch profiling part 3: attention", section "构建因果掩码":
  *            true entries keep their score).  Read only.
- *   bits     device pointer, [rows, ceil(Nk / 64)] 64-bit words, 8-byte aligned;
- *            written: bit j % 64 of word j / 64 of row r = (mask[r, j] != 0);
- *            bits past Nk are 0.
- *   rows, Nk  >= 1.
+ *   bits     device pointer, [heads, Nq, W] 64-bit words (W = ceil(Nk / 64)),
+ *            8-byte aligned; written: bit j % 64 of word j / 64 of row r =
+ *            (mask[.., r, j] != 0); bits past Nk are 0.
+ *   tiles    NULL, or a device pointer to [heads, ceil(Nq / 256), ceil(W / 64)]
+ *            64-bit words, 8-byte aligned; written: bit u % 64 of word u / 64 of
+ *            (head, t) = 1 iff some row of rows 256 t .. 256 t + 255 has a
+ *            visible key in keys 64 u .. 64 u + 63 (the tile summary of
+ *            attn_fwd_masked).
+ *   heads, Nq, Nk  >= 1.
  *   stream   HIP stream the work is enqueued on.
  *
  * The packed mask can be reused by any number of attn_fwd_masked calls.
- * Errors: ATTN_EINVAL (NULL pointer, rows or Nk < 1, bits misaligned, bits
- * overlapping mask), ATTN_EUNSUPPORTED (more than 2^40 words), ATTN_EHIP
- * (launch failure).  Asynchronous like attn_fwd.
+ * Errors: ATTN_EINVAL (NULL mask or bits, a size < 1, bits or tiles misaligned,
+ * outputs overlapping the mask or each other), ATTN_EUNSUPPORTED (more than
+ * 2^40 words), ATTN_EHIP (launch failure).  Asynchronous like attn_fwd.
  */
-ATTN_API int attn_mask_pack(const void *mask, void *bits, long long rows, int Nk,
-                            hipStream_t stream);
+ATTN_API int attn_mask_pack(const void *mask, void *bits, void *tiles, long long heads, int Nq,
+                            int Nk, hipStream_t stream);
 
 /*
  * attn_bwd — gradients of attention for B*H independent heads.

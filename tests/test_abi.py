@@ -129,11 +129,13 @@ def test_bwd_outputs_right_after_inputs_are_fine():
 
 
 # attn_fwd_masked and attn_mask_pack: host checks only (fake addresses, nothing launched).
-MB = 11 << 40
-GOOD_M = dict(q=Q, k=K, v=V, mask=MB, sb=0, sh=0, o=O, lse=L, B=2, H=3, Nq=100, Nk=300, d=64,
+MB, MT = 11 << 40, 12 << 40
+GOOD_M = dict(q=Q, k=K, v=V, mask=MB, tiles=MT, sb=3, sh=1, o=O, lse=L, B=2, H=3, Nq=100, Nk=300, d=64,
               scale=0.125, causal=1, dtype=2, stream=0)
-M_ORDER = ["q", "k", "v", "mask", "sb", "sh", "o", "lse", "B", "H", "Nq", "Nk", "d", "scale",
+M_ORDER = ["q", "k", "v", "mask", "tiles", "sb", "sh", "o", "lse", "B", "H", "Nq", "Nk", "d", "scale",
            "causal", "dtype", "stream"]
+MASK_BYTES = 6 * 100 * 5 * 8    # 6 mask heads of 100 rows of 5 words
+TILE_BYTES = 6 * 1 * 1 * 8      # 6 mask heads of 1 tile of 1 word
 
 
 def call_m(**kw):
@@ -147,34 +149,41 @@ def call_m(**kw):
     dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(Nk=-3), dict(d=0),
     dict(dtype=3), dict(causal=2), dict(scale=float("nan")),
     dict(q=Q + 8), dict(k=K + 4), dict(o=O + 2), dict(lse=L + 1), dict(mask=MB + 4),
+    dict(tiles=MT + 4), dict(mask=0),        # tiles without a mask
     dict(sb=-1), dict(sh=-5),
     dict(o=Q), dict(o=K + 16), dict(lse=V + 64), dict(lse=O + 16),
-    dict(o=MB), dict(lse=MB + 8 * 5 * 99),   # inside the mask words read (Nq rows of 5 words)
-    dict(o=V - 16),                          # o ends inside v (v holds Nk rows)
+    dict(o=MB), dict(lse=MB + MASK_BYTES - 8),   # inside the mask words read
+    dict(lse=MT + TILE_BYTES - 4),               # inside the tile summary
+    dict(o=V - 16),                              # o ends inside v (v holds Nk rows)
 ], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
 def test_masked_invalid_arguments(kw):
     assert call_m(**kw) == ea.ATTN_EINVAL
 
 
-@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(B=65536, H=65536, Nq=1, Nk=1, d=64),
-                                dict(sb=1 << 41), dict(Nq=1 << 20, Nk=1 << 20)])
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(B=65536, H=65536, Nq=1, Nk=1, d=64, sb=0, sh=0),
+                                dict(sb=1 << 32), dict(Nq=1 << 20, Nk=1 << 20, sb=0, sh=0),
+                                dict(Nk=4097 * 64, Nq=1, sb=0, sh=0)])  # unit list too long for LDS
 def test_masked_unsupported(kw):
     assert call_m(**kw) == ea.ATTN_EUNSUPPORTED
 
 
 def test_masked_without_mask_ignores_strides():
-    # no mask: the strides are not examined (a bad dtype is what is reported)
-    assert call_m(mask=0, sb=-1, sh=-1, dtype=9) == ea.ATTN_EINVAL
+    # no mask and no tiles: the strides are not examined (a bad dtype is what is reported)
+    assert call_m(mask=0, tiles=0, sb=-1, sh=-1, dtype=9) == ea.ATTN_EINVAL
 
 
 def test_masked_lse_right_after_mask_is_fine_to_check():
-    # the mask spans (B-1) sb + (H-1) sh + Nq * 5 words; lse right after it does not overlap
-    assert call_m(lse=MB + 8 * 5 * 100, dtype=7) == ea.ATTN_EINVAL  # rejected for the dtype only
+    # mask heads 0 .. (B-1) sb + (H-1) sh = 5 are read; lse right after them does not overlap
+    assert call_m(lse=MB + MASK_BYTES, dtype=7) == ea.ATTN_EINVAL  # rejected for the dtype only
+    assert call_m(lse=MT + TILE_BYTES, dtype=7) == ea.ATTN_EINVAL
 
 
 @pytest.mark.parametrize("args", [
-    (0, MB, 4, 100), (Q, 0, 4, 100), (Q, MB, 0, 100), (Q, MB, 4, 0), (Q, MB + 4, 4, 100),
-    (Q, Q + 8, 4, 100),  # bits inside the mask bytes
+    (0, MB, MT, 4, 100, 100), (Q, 0, MT, 4, 100, 100), (Q, MB, MT, 0, 100, 100),
+    (Q, MB, MT, 4, 0, 100), (Q, MB, MT, 4, 100, 0), (Q, MB + 4, MT, 4, 100, 100),
+    (Q, MB, MT + 2, 4, 100, 100),
+    (Q, Q + 8, MT, 4, 100, 100),      # bits inside the mask bytes
+    (Q, MB, MB + 64, 4, 100, 100),    # tiles inside the bits
 ])
 def test_mask_pack_invalid_arguments(args):
     assert ea.attn_mask_pack_ptr(*args, 0) == ea.ATTN_EINVAL

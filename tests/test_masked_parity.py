@@ -141,19 +141,50 @@ def test_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("rows,nk", [(1, 1), (3, 64), (5, 65), (7, 300), (64, 1000)])
-def test_mask_pack_bits(rows, nk):
-    """attn_mask_pack against bit packing done on the host (bit-exact)."""
+@pytest.mark.parametrize("heads,rows,nk", [(1, 1, 1), (1, 3, 64), (2, 5, 65), (1, 7, 300), (3, 64, 1000),
+                                           (2, 300, 200), (1, 513, 4200)])
+def test_mask_pack_bits(heads, rows, nk):
+    """attn_mask_pack against bit packing and tile summaries done on the host (bit-exact).
+    Sparse masks, so that empty units and empty tiles occur."""
     g = torch.Generator().manual_seed(rows * 1000 + nk)
-    m = torch.randint(0, 3, (1, 1, rows, nk), generator=g, dtype=torch.uint8)  # 0, 1, 2 (nonzero = on)
-    bits = ea.pack_mask(m.to(DEV)).cpu().numpy().view(np.uint64)
+    m = torch.randint(0, 3, (heads, 1, rows, nk), generator=g, dtype=torch.uint8)  # 0, 1, 2 (nonzero = on)
+    m *= (torch.rand((heads, 1, rows, nk), generator=g) < 0.002).to(torch.uint8)
+    packed = ea.pack_mask(m.to(DEV))
+    bits = packed.bits.cpu().numpy().view(np.uint64)
+    tiles = packed.tiles.cpu().numpy().view(np.uint64)
     W = (nk + 63) // 64
-    on = np.zeros((rows, W * 64), dtype=np.uint64)
-    on[:, :nk] = (m.numpy()[0, 0] != 0)
-    want = np.zeros((rows, W), dtype=np.uint64)
+    on = np.zeros((heads, rows, W * 64), dtype=np.uint64)
+    on[:, :, :nk] = (m.numpy()[:, 0] != 0)
+    want = np.zeros((heads, rows, W), dtype=np.uint64)
     for j in range(W * 64):
-        want[:, j // 64] |= on[:, j] << np.uint64(j % 64)
-    assert np.array_equal(bits[0, 0], want)
+        want[:, :, j // 64] |= on[:, :, j] << np.uint64(j % 64)
+    assert np.array_equal(bits[:, 0], want)
+    nt, tw = (rows + 255) // 256, (W + 63) // 64
+    unit_any = np.zeros((heads, nt, tw * 64), dtype=np.uint64)
+    for t in range(nt):
+        unit_any[:, t, :W] = (want[:, 256 * t:256 * t + 256] != 0).any(axis=1)
+    want_t = np.zeros((heads, nt, tw), dtype=np.uint64)
+    for u in range(tw * 64):
+        want_t[:, :, u // 64] |= unit_any[:, :, u] << np.uint64(u % 64)
+    assert np.array_equal(tiles[:, 0], want_t)
+
+
+@pytest.mark.parametrize("kind,kw", [("blocks", dict(p=0.2)), ("window", dict(w=300)),
+                                     ("bernoulli", dict(p=0.001)), ("padding", {})])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unit_skipping_changes_nothing(kind, kw, causal):
+    """With the tile summary the kernel skips units no row of a query tile sees; a
+    skipped unit would only have added exact zeros, so the results are bitwise those
+    of the same kernel walking every unit (and both match the oracle)."""
+    q, k, v = random_qkv_lens(2, 2, 700, 1500, 128, "bf16", seed=81)
+    mask = random_mask(kind, 2, 1, 700, 1500, seed=82, **kw)
+    parity(q, k, v, mask, causal, float(np.float32(128 ** -0.5)), "bf16", f"skipping {kind}")
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    packed = ea.pack_mask(mask.to(DEV))
+    o1, l1 = ea.attn_fwd_masked(qd, kd, vd, mask_bits=packed, causal=causal)
+    o2, l2 = ea.attn_fwd_masked(qd, kd, vd, mask_bits=packed.bits, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_full_size_sliding_window():
