@@ -94,19 +94,29 @@ hipError_t dispatch_mode(const FwdArgs &a, int bh, int causal, int dtype, hipStr
     return dispatch_dtype<D, true, attn::kFwdPlain>(a, bh, dtype, stream);
 }
 
-// Packs a byte mask [rows, Nk] into bits [rows, ceil(Nk / 64)]: one wave per
-// 64-bit word, each lane reading one key's byte; the wave's ballot is the word.
+// Packs a byte mask [rows, Nk] into bits [rows, ceil(Nk / 64)]: a wave makes
+// PACK_WORDS consecutive 64-bit words per pass, each lane reading one key's byte of
+// each (independent loads in flight); the wave's ballot is the word.
+constexpr int PACK_WORDS = 8;
 __global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t *mask, uint64_t *bits, long long words,
                                                              int Nk, int w_per_row) {
     const int lane = threadIdx.x & 63;
     const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const long long n_waves = (long long)gridDim.x * 4;
-    for (long long i = wave; i < words; i += n_waves) {
-        const long long r = i / w_per_row;
-        const int key = (int)(i - r * w_per_row) * 64 + lane;
-        const bool on = key < Nk && mask[r * Nk + key] != 0;
-        const uint64_t word = __builtin_amdgcn_ballot_w64(on);
-        if (lane == 0) bits[i] = word;
+    for (long long i0 = wave * PACK_WORDS; i0 < words; i0 += n_waves * PACK_WORDS) {
+        bool on[PACK_WORDS];
+#pragma unroll
+        for (int t = 0; t < PACK_WORDS; ++t) {
+            const long long i = i0 + t;
+            const long long r = i / w_per_row;
+            const int key = (int)(i - r * w_per_row) * 64 + lane;
+            on[t] = i < words && key < Nk && mask[r * Nk + key] != 0;
+        }
+#pragma unroll
+        for (int t = 0; t < PACK_WORDS; ++t) {
+            const uint64_t word = __builtin_amdgcn_ballot_w64(on[t]);
+            if (lane == 0 && i0 + t < words) bits[i0 + t] = word;
+        }
     }
 }
 
@@ -128,7 +138,8 @@ __global__ __launch_bounds__(256) void attn_mask_tiles_kernel(const uint64_t *bi
         if (u < W) {
             const int r0 = t * attn::kMaskTileRows, r1 = min(r0 + attn::kMaskTileRows, Nq);
             const uint64_t *col = bits + (head * Nq + r0) * (long long)W + u;
-            for (int r = r0; r < r1; ++r, col += W) any |= *col;
+#pragma unroll 16
+            for (int r = r0; r < r1; ++r, col += W) any |= *col;  // independent loads
         }
         const uint64_t word = __builtin_amdgcn_ballot_w64(any != 0);
         if (lane == 0) tiles[i] = word;
@@ -265,7 +276,7 @@ extern "C" ATTN_API int attn_mask_pack(const void *mask, void *bits, void *tiles
     if (overlaps(bits, words * 8, mask, rows * (uint64_t)Nk)) return ATTN_EINVAL;
     if (tiles && (overlaps(tiles, twords * 8, mask, rows * (uint64_t)Nk) || overlaps(tiles, twords * 8, bits, words * 8)))
         return ATTN_EINVAL;
-    const uint64_t blocks = (words + 3) / 4;
+    const uint64_t blocks = (words + 4 * PACK_WORDS - 1) / (4 * PACK_WORDS);
     hipError_t e = launch(&attn_mask_pack_kernel, (int)(blocks < 65536 ? blocks : 65536), 256, 0, stream,
                           static_cast<const uint8_t *>(mask), static_cast<uint64_t *>(bits), (long long)words, Nk,
                           (int)w);
