@@ -121,6 +121,15 @@ template <> struct Mfma<_Float16> {
     }
 };
 
+// Lane id (0..63) computed where it is used: volatile, so the compiler neither hoists
+// it nor keeps values derived from it live across the key loop (where it would
+// spill them, and a spill reload waits for every load in flight, DMA included).
+__device__ __forceinline__ uint32_t lane_id_here() {
+    uint32_t x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 // Swap bits 2 and 3 of a row index inside a 32-row block (an involution).
 __device__ __forceinline__ int swap_bits23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -241,7 +250,8 @@ struct MfmaFwd {
         uint32_t vaddr[DB];      // LDS address of this lane's V^T fragment for d block db (stage 0)
         float c;                 // scale * log2(e), >= 0
         int r0, Nk, off, l32, g; // first row of the wave, key length, causal offset, lane coordinates
-        uint32_t mrow;           // LDS offset of the lane's row in a mask stage (MASK)
+        uint32_t mrow0;          // LDS address of the workgroup-relative row r0 in mask stage 0
+                                 // (MASK; wave-uniform: the lane adds 8 * (lane % 32))
     };
 
     // ------------------------------------------------------------ building blocks
@@ -328,10 +338,16 @@ struct MfmaFwd {
     // with r = 2 h + (i >> 3), i.e. byte 2 r + g of the row word; key offsets grow
     // with the bit index, so the position limit keeps a prefix of the bits.
     static __device__ __forceinline__ uint32_t visible_bits(const State &S, int k0, uint32_t moff) {
-        const u32x2_t wd = *(const __attribute__((address_space(3))) u32x2_t *)(uintptr_t)(S.mrow + moff);
-        const uint32_t lo = wd[0] >> (8 * S.g), hi = wd[1] >> (8 * S.g);
+        // the lane's row address and key limit from the lane id (no register is kept
+        // for them across the loop)
+        const uint32_t ln = lane_id_here();
+        const int l32 = (int)(ln & 31u), g = (int)(ln >> 5);
+        const uint32_t addr = S.mrow0 + moff + 8u * (uint32_t)l32;
+        const u32x2_t wd = *(const __attribute__((address_space(3))) u32x2_t *)(uintptr_t)addr;
+        const uint32_t lo = wd[0] >> (8 * g), hi = wd[1] >> (8 * g);
         const uint32_t bits = (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi & 0xff0000u) << 8);
-        const int lim = vis_limit(S, k0);
+        const int last = CAUSAL ? min(S.r0 + l32 + S.off, S.Nk - 1) : S.Nk - 1;
+        const int lim = last - k0 - 8 * g;
         int n = 0;  // registers whose key offset is <= lim: a prefix of the bit order
 #pragma unroll
         for (int r = 0; r < 4; ++r) n += min(max(lim - 16 * r + 1, 0), 8);
@@ -444,9 +460,12 @@ struct MfmaFwd {
         // head then start close together and read its K and V units from the L2 at
         // nearly the same time.  Otherwise the rank is simply longest-first over all
         // heads.  Non-causal tiles are all equal: each XCD takes a contiguous range of
-        // (head, tile) pairs, so consecutive tiles of a head share its L2.
+        // (head, tile) pairs, so consecutive tiles of a head share its L2.  With a
+        // caller's mask the tiles skip different numbers of units; they take the causal
+        // order (later query tiles first), which starts the longest tiles first for the
+        // usual lower-triangular and banded masks and costs nothing for uniform ones.
         int bh, qt;
-        if (CAUSAL) {
+        if (CAUSAL || MASK) {
             const int nq = a.n_qtiles, n_bh = a.total / nq, per = n_bh >> 3;
             if ((n_bh & 15) == 0) {
                 const int hg = (per & 3) == 0 ? 4 : 2;
@@ -544,11 +563,12 @@ struct MfmaFwd {
             const int b = bh / a.H, hh = bh - b * a.H;
             mhead = (size_t)b * (size_t)a.mask_sb + (size_t)hh * (size_t)a.mask_sh;
             Mh = a.mask + mhead * (size_t)Nq * (size_t)a.mask_w;
-            S.mrow = lds0 + M_BASE + (uint32_t)(S.r0 - qt * BR + l32) * 8u;
+            S.mrow0 = lds0 + M_BASE + (uint32_t)(S.r0 - qt * BR) * 8u;
         }
-        auto mask_src = [&]() -> uint32_t {
-            const int q = min(qt * BR + ((w * 64 + (l32 + 32 * g)) >> 1), Nq - 1);
-            return (uint32_t)q * (uint32_t)a.mask_w * 8u + 4u * (uint32_t)(l32 & 1);
+        auto mask_src = [&]() -> uint32_t {  // from the lane id, recomputed per load
+            const int ln = (int)lane_id_here();
+            const int q = min(qt * BR + ((w * 64 + ln) >> 1), Nq - 1);
+            return (uint32_t)q * (uint32_t)a.mask_w * 8u + 4u * (uint32_t)(ln & 1);
         };
 
         // Units of BU keys this workgroup and this wave need: causal rows see keys up
@@ -732,6 +752,31 @@ struct MfmaFwd {
                 barrier_end();
             }
         }
+        // MASK: the units of positions u .. u + 3 ride in a scalar shift register
+        // (lst[j] = unit of position min(u + j, nu_wg - 1)); each step reads one new
+        // list entry during its softmax phase and takes it after the barrier that ends
+        // the step (which has waited for LDS), so no lookup latency lands on a phase.
+        int lst[STAGES];
+        if (MASK) {
+#pragma unroll
+            for (int j = 0; j < STAGES; ++j) lst[j] = unit_at(min(j, nu_wg - 1));
+        }
+        auto masked_step_bits = [&]() {
+            const Units un{lst[STAGES - 1], lst[STAGES - 2]};
+            issue_mask(un, u + STAGES - 1);
+            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
+            barrier_mid();
+            const int next = min(u + STAGES, nu_wg - 1);
+            int pf = next;
+            if (use_list) pf = *(const __attribute__((address_space(3))) int *)(uintptr_t)(lds0 + LIST_BASE + 4 * next);
+            kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
+            soft<true, false>(S, s, pk, lst[0] * BU, (u % STAGES) * MUNIT_B);
+            pin_soft();
+            barrier_end();
+#pragma unroll
+            for (int j = 0; j + 1 < STAGES; ++j) lst[j] = lst[j + 1];
+            lst[STAGES - 1] = __builtin_amdgcn_readfirstlane(pf);
+        };
         auto masked_step = [&]() {
             const Units un = units(u + STAGES - 1);
             issue_mask(un, u + STAGES - 1);
@@ -750,7 +795,9 @@ struct MfmaFwd {
         // masked steps nm .. nu - 1: every unit with a caller's mask; one or two where
         // the causal diagonal of the wave's 32 rows may cross a unit boundary; one in
         // kFwdPlain
-        if (MODE != kFwdPlain) {
+        if (MASK) {
+            for (; u < nu; ++u) masked_step_bits();
+        } else if (MODE != kFwdPlain) {
             for (; u < nu; ++u) masked_step();
         } else if (u < nu) {
             masked_step();
@@ -780,12 +827,15 @@ struct MfmaFwd {
         // of a row hold alternate groups of 4 columns.  One exchange between them (lane ^ 32,
         // same row) gives every lane 8 consecutive columns: 16-byte stores, half as many
         // store instructions as storing each lane's own groups of 4.
-        const int q = S.r0 + l32;
+        // (MASK: lane coordinates recomputed, so that they are not live across the loop)
+        const int lane_e = MASK ? (int)lane_id_here() : lane;
+        const int l32e = lane_e & 31, ge = lane_e >> 5;
+        const int q = S.r0 + l32e;
         const float ltot = lane_swap32_add(S.lsum);
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         auto partner = [&](uint32_t x) -> uint32_t {  // x of lane ^ 32
             const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-            return g ? r[0] : r[1];
+            return ge ? r[0] : r[1];
         };
 #pragma unroll
         for (int b = 0; b < DB; ++b)
@@ -800,15 +850,15 @@ struct MfmaFwd {
                 }
                 // lane half 0 keeps group k and receives the other half's group k; half 1
                 // keeps group k + 1 and receives the other half's group k + 1
-                const u32x2_t give = g ? mine[0] : mine[1];
+                const u32x2_t give = ge ? mine[0] : mine[1];
                 const u32x2_t got = {partner(give[0]), partner(give[1])};
-                const u32x2_t lo = g ? got : mine[0], hi = g ? mine[1] : got;
+                const u32x2_t lo = ge ? got : mine[0], hi = ge ? mine[1] : got;
                 if (q < Nq) {
-                    uint16_t *dst = static_cast<uint16_t *>(a.o) + head + (size_t)q * D + b * 32 + 8 * (k + g);
+                    uint16_t *dst = static_cast<uint16_t *>(a.o) + head + (size_t)q * D + b * 32 + 8 * (k + ge);
                     *reinterpret_cast<u32x4_t *>(dst) = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
                 }
             }
-        if (q < Nq && g == 0) a.lse[(size_t)bh * Nq + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
+        if (q < Nq && ge == 0) a.lse[(size_t)bh * Nq + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
     }
 };
 
