@@ -761,16 +761,19 @@ struct MfmaFwd {
 #pragma unroll
             for (int j = 0; j < STAGES; ++j) lst[j] = unit_at(min(j, nu_wg - 1));
         }
-        auto masked_step_bits = [&]() {
+        // st: u mod STAGES as a compile-time constant (ring stages as immediates), or -1
+        auto masked_step_bits = [&](auto st) {
+            constexpr int ST = decltype(st)::value;
+            const int sg = ST >= 0 ? ST : u % STAGES;
             const Units un{lst[STAGES - 1], lst[STAGES - 2]};
             issue_mask(un, u + STAGES - 1);
-            gemm(S, s, pk, kf, ((u + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
+            gemm(S, s, pk, kf, ((sg + STAGES - 1) % STAGES) * UNIT_B, [&](int j) { issue_part(un, u + STAGES - 1, j); });
             barrier_mid();
             const int next = min(u + STAGES, nu_wg - 1);
             int pf = next;
             if (use_list) pf = *(const __attribute__((address_space(3))) int *)(uintptr_t)(lds0 + LIST_BASE + 4 * next);
-            kload(S, kf, ((u + 1) % STAGES) * UNIT_B);
-            soft<true, false>(S, s, pk, lst[0] * BU, (u % STAGES) * MUNIT_B);
+            kload(S, kf, ((sg + 1) % STAGES) * UNIT_B);
+            soft<true, false>(S, s, pk, lst[0] * BU, sg * MUNIT_B);
             pin_soft();
             barrier_end();
 #pragma unroll
@@ -795,8 +798,18 @@ struct MfmaFwd {
         // masked steps nm .. nu - 1: every unit with a caller's mask; one or two where
         // the causal diagonal of the wave's 32 rows may cross a unit boundary; one in
         // kFwdPlain
-        if (MASK) {
-            for (; u < nu; ++u) masked_step_bits();
+        if (MASK) {  // from unit 0: unrolled by four so that the ring stage is an immediate
+            for (; u + STAGES <= nu; ) {
+                masked_step_bits(std::integral_constant<int, 0>());
+                ++u;
+                masked_step_bits(std::integral_constant<int, 1>());
+                ++u;
+                masked_step_bits(std::integral_constant<int, 2>());
+                ++u;
+                masked_step_bits(std::integral_constant<int, 3>());
+                ++u;
+            }
+            for (; u < nu; ++u) masked_step_bits(std::integral_constant<int, -1>());
         } else if (MODE != kFwdPlain) {
             for (; u < nu; ++u) masked_step();
         } else if (u < nu) {
