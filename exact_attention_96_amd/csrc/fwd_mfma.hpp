@@ -373,10 +373,7 @@ struct MfmaFwd {
                     const int i0 = 8 * kc + 2 * e;
                     float p0 = fast_exp2(fmaf(s[h][i0], S.c, nm));
                     float p1 = fast_exp2(fmaf(s[h][i0 + 1], S.c, nm));
-                    if (MASK) {
-                        p0 = vis_bit(vm, 16 * h + i0) ? p0 : 0.f;
-                        p1 = vis_bit(vm, 16 * h + i0 + 1) ? p1 : 0.f;
-                    } else if (MASKED) {
+                    if (MASKED && !MASK) {  // (MASK: hidden scores are already -inf)
                         p0 = key_off(h, i0) <= lim ? p0 : 0.f;
                         p1 = key_off(h, i0 + 1) <= lim ? p1 : 0.f;
                     }
@@ -400,6 +397,14 @@ struct MfmaFwd {
     template <bool MASKED, bool FIRST>
     static __device__ __forceinline__ void soft(State &S, f32x16_t (&s)[2], Packed &pk, int k0, uint32_t moff = 0) {
         const uint32_t vm = MASK ? visible_bits(S, k0, moff) : 0u;
+        if (MASK && __builtin_amdgcn_ballot_w64(vm != 0xffffffffu)) {
+            // some score of the unit is hidden: set it to -inf in place (c > 0 here, so
+            // its exponential is 0); wholly visible units skip this
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[h][i] = vis_bit(vm, 16 * h + i) ? s[h][i] : -INFINITY;
+        }
         auto move_reference = [&](bool rescale) {
             const int lim = MASKED && !MASK ? vis_limit(S, k0) : 0;
             float mx = -INFINITY;
@@ -407,9 +412,7 @@ struct MfmaFwd {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, MASK     ? (vis_bit(vm, 16 * h + i) ? s[h][i] : -INFINITY)
-                                   : MASKED ? (key_off(h, i) <= lim ? s[h][i] : -INFINITY)
-                                            : s[h][i]);
+                    mx = fmaxf(mx, MASKED && !MASK ? (key_off(h, i) <= lim ? s[h][i] : -INFINITY) : s[h][i]);
             mx = lane_swap32_max(mx);
             const float mt = mx == -INFINITY ? -INFINITY : mx * S.c;
             const float m_new = fmaxf(S.m_ref, mt);
@@ -507,6 +510,10 @@ struct MfmaFwd {
             S.c = -S.c;
             qsign = 0x80008000u;
         }
+        // MASK writes -inf into hidden scores: keep c > 0 so that -inf * c stays -inf
+        // (a scale of 0 becomes 1e-30, which moves no finite score by an ulp of the
+        // reference it is added to)
+        if (MASK) S.c = fmaxf(S.c, 1e-30f);
 
         // Q^T as the B operand: lane holds Q[q][16 cc + 8 g .. +7] for its row q
         // (rows past the end read row Nq-1 and are zeroed).

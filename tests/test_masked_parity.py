@@ -206,3 +206,13 @@ def test_full_size_sliding_window():
         compare(o[b, h, rows], lse[b, h, rows], o_ref[0, 0], lse_ref[0, 0], "bf16",
                 f"window head ({b},{h})")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 1.0])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 64)])
+def test_masked_scales(scale, dtype, d):
+    """Scale 0 (every visible key weighs the same: o is the mean of the visible values,
+    lse the log of their count), a negative scale and a large one, under a mask."""
+    q, k, v = random_qkv_lens(2, 2, 200, 333, d, dtype, seed=91)
+    mask = random_mask("bernoulli", 1, 2, 200, 333, seed=92, p=0.3)
+    parity(q, k, v, mask, True, scale, dtype, f"masked scale {scale}")
