@@ -13,7 +13,9 @@ section "朴素注意力" (naive attention); and its backward (dQ, dK, dV of a l
 with gradient dO) from "Understand FlashAttention", section "反向传播"; and the
 general-mask form (boolean or additive mask, unequal query and key lengths,
 safe softmax) from "PyTorch profiling part 3", sections "构建因果掩码" and
-"安全 softmax".  This module only marshals arrays.
+"安全 softmax"; and causal linear attention (phi(x) = elu(x) + 1 similarity,
+causal dot product, normaliser) from the hqwc.cn notes on the fast-transformers
+linear attention kernels, sections 0x0-0x2.  This module only marshals arrays.
 
 Pins (tests/test_oracle.py) tie it to facts the pages and the mathematics fix;
 every function here is pinned (none is "parity unpinned").
@@ -71,6 +73,9 @@ class OracleLib:
         lib.oracle_attn_masked_f64.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, i64, i64, i64, i64,
                                                i64, ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_masked_f64.restype = ctypes.c_int
+        lib.oracle_linattn_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
+                                           ctypes.c_double]
+        lib.oracle_linattn_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -177,6 +182,25 @@ class OracleLib:
             raise RuntimeError(f"oracle_attn_masked_f64 failed with status {rc}")
         return o, lse
 
+    def linear_attn(self, q, k, v, feature_map: bool = True, eps: float = 1e-6):
+        """Causal linear attention, out [B, H, N, M] for q, k [B, H, N, E], v [B, H, N, M].
+
+        feature_map=False: the causal dot product out_j = sum_{t<=j} (q_j . k_t) v_t;
+        True: phi = elu + 1 on q and k, and out_j = that product of phi(q), phi(k), v
+        times 1 / (phi(q_j) . sum_{t<=j} phi(k_t) + eps).
+        """
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or v.shape[:3] != q.shape[:3]:
+            raise ValueError("q, k [B, H, N, E] and v [B, H, N, M] expected")
+        B, H, N, E = q.shape
+        M = v.shape[3]
+        out = np.empty((B, H, N, M), dtype=np.float64)
+        rc = self.lib.oracle_linattn_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B * H, N, E, M,
+                                         int(bool(feature_map)), float(eps))
+        if rc:
+            raise RuntimeError(f"oracle_linattn_f64 failed with status {rc}")
+        return out
+
 
 def _f64(x) -> np.ndarray:
     """Exact widening of a torch tensor or array to a C-contiguous fp64 array."""
@@ -221,3 +245,7 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool):
 
 def attn_masked(q, k, v, scale: float, causal: bool, mask=None, kind: str = "bool"):
     return default().attn_masked(q, k, v, scale, causal, mask, kind)
+
+
+def linear_attn(q, k, v, feature_map: bool = True, eps: float = 1e-6):
+    return default().linear_attn(q, k, v, feature_map, eps)

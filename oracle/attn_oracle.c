@@ -395,6 +395,81 @@ int oracle_attn_masked_f64(const double *q, const double *k, const double *v,
 }
 
 /* Number of OpenMP threads a parallel region of this library will use. */
+/*
+ * Causal linear attention (another method, from the hqwc.cn notes on the
+ * fast-transformers linear attention CUDA kernels, "Transformers are RNNs"):
+ *
+ *   section 0x0: the softmax similarity exp(q.k / sqrt(D)) is replaced by a
+ *   kernel sim(q, k) = phi(q) . phi(k) with phi(x) = elu(x) + 1;
+ *   section 0x1: the CausalLinearAttention module applies phi to the queries
+ *   and keys, computes the normaliser Z_j = 1 / (phi(q_j) . sum_{t<=j}
+ *   phi(k_t) + eps) and returns causal_dot_product(phi(Q), phi(K), V) * Z;
+ *   section 0x2: causal_dot_product computes V'_j = sum_{t<=j} (q_j . k_t) v_t.
+ *
+ * feature_map = 0 computes the causal dot product alone (q, k used as given,
+ * no normaliser); feature_map = 1 the whole module.  Written as the definition:
+ * for each query row j a plain sum over the keys t <= j (O(N^2) per head), not
+ * the running-state recurrence of the page's CPU and CUDA code.
+ *   q, k : [BH, N, E]; v : [BH, N, M]; out : [BH, N, M] (written).
+ */
+static double elu_plus_one(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+int oracle_linattn_f64(const double *q, const double *k, const double *v,
+                       double *out, int64_t BH, int64_t N, int64_t E, int64_t M,
+                       int feature_map, double eps)
+{
+    if (!q || !k || !v || !out || BH < 1 || N < 1 || E < 1 || M < 1) return 1;
+    if (feature_map != 0 && feature_map != 1) return 1;
+    const int64_t nq = BH * N * E;
+    double *fq = malloc(sizeof(double) * (size_t)nq);
+    double *fk = malloc(sizeof(double) * (size_t)nq);
+    if (!fq || !fk) { free(fq); free(fk); return 2; }
+    for (int64_t x = 0; x < nq; ++x) {   /* the feature map, elementwise */
+        fq[x] = feature_map ? elu_plus_one(q[x]) : q[x];
+        fk[x] = feature_map ? elu_plus_one(k[x]) : k[x];
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *num = malloc(sizeof(double) * (size_t)M);
+        double *ksum = malloc(sizeof(double) * (size_t)E);
+        if (!num || !ksum) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < BH * N; ++r) {
+            if (!num || !ksum) continue;
+            const int64_t h = r / N, j = r % N;
+            const double *qj = fq + r * E;
+            for (int64_t m = 0; m < M; ++m) num[m] = 0.0;
+            for (int64_t e = 0; e < E; ++e) ksum[e] = 0.0;
+            for (int64_t t = 0; t <= j; ++t) {   /* causal: keys t <= j */
+                const double *kt = fk + (h * N + t) * E;
+                const double *vt = v + (h * N + t) * M;
+                double sim = 0.0;
+                for (int64_t e = 0; e < E; ++e) sim += qj[e] * kt[e];
+                for (int64_t m = 0; m < M; ++m) num[m] += sim * vt[m];
+                for (int64_t e = 0; e < E; ++e) ksum[e] += kt[e];
+            }
+            double *oj = out + r * M;
+            if (feature_map) {
+                double den = 0.0;   /* phi(q_j) . sum_{t<=j} phi(k_t) */
+                for (int64_t e = 0; e < E; ++e) den += qj[e] * ksum[e];
+                const double z = 1.0 / (den + eps);
+                for (int64_t m = 0; m < M; ++m) oj[m] = num[m] * z;
+            } else {
+                for (int64_t m = 0; m < M; ++m) oj[m] = num[m];
+            }
+        }
+        free(num);
+        free(ksum);
+    }
+    free(fq);
+    free(fk);
+    return failed ? 2 : 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -590,4 +590,134 @@ def pin_masked_torch_sdpa(orc):
             _close(lse, torch.logsumexp(sb, dim=-1).numpy(), 1e-12, f"sdpa masked lse {kind}")
 
 
+# ---------------------------------------------------------------- causal linear attention
+# (hqwc.cn notes on the fast-transformers kernels, sections 0x0-0x2)
+
+def _lin_recurrence(q, k, v, feature_map, eps):
+    """The running-state form the page's CPU code uses (a separately written route):
+    S += k_t v_t^T, z += k_t, then out_t = q_t S (/ (q_t . z + eps))."""
+    phi = (lambda x: np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))) if feature_map else (lambda x: x)
+    q, k = phi(q), phi(k)
+    B, H, N, E = q.shape
+    M = v.shape[3]
+    out = np.empty((B, H, N, M))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((E, M))
+            z = np.zeros(E)
+            for t in range(N):
+                S += np.outer(k[b, h, t], v[b, h, t])
+                z += k[b, h, t]
+                o = q[b, h, t] @ S
+                out[b, h, t] = o / (q[b, h, t] @ z + eps) if feature_map else o
+    return out
+
+
+def pin_linear_recurrence(orc):
+    """The definition (oracle) equals the running-state recurrence (page section 0x2's CPU
+    loop: outer product into the state, then the query times the state), both forms."""
+    rng = np.random.default_rng(61)
+    for (B, H, N, E, M) in [(1, 1, 1, 3, 2), (2, 3, 17, 8, 5), (1, 2, 40, 16, 32)]:
+        q, k = rng.standard_normal((2, B, H, N, E))
+        v = rng.standard_normal((B, H, N, M))
+        for fm in (False, True):
+            _close(orc.linear_attn(q, k, v, fm, 1e-6), _lin_recurrence(q, k, v, fm, 1e-6), 1e-11,
+                   f"linear recurrence fm={fm} {B,H,N,E,M}")
+
+
+def pin_linear_torch_einsum(orc):
+    """torch CPU fp64 with the page's module written as library calls: Z = 1/(einsum(Q,
+    K.cumsum) + eps), the causal product as tril(Q K^T) V, phi = F.elu + 1."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(62)
+    B, H, N, E, M = 2, 2, 33, 16, 24
+    q, k = rng.standard_normal((2, B, H, N, E))
+    v = rng.standard_normal((B, H, N, M))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    fq, fk = F.elu(tq) + 1, F.elu(tk) + 1
+    prod = torch.matmul(torch.tril(torch.matmul(fq, fk.transpose(-1, -2))), tv)
+    z = 1.0 / (torch.einsum("bhle,bhle->bhl", fq, fk.cumsum(2)) + 1e-6)
+    _close(orc.linear_attn(q, k, v, True, 1e-6), (prod * z[..., None]).numpy(), 1e-12, "linear torch module")
+    raw = torch.matmul(torch.tril(torch.matmul(tq, tk.transpose(-1, -2))), tv)
+    _close(orc.linear_attn(q, k, v, False), raw.numpy(), 1e-12, "linear torch product")
+
+
+def pin_linear_closed_forms(orc):
+    """Row 0 sees key 0 alone: raw out_0 = (q_0 . k_0) v_0; with the feature map
+    out_0 = s v_0 / (s + eps), s = phi(q_0) . phi(k_0).  phi(x) = x + 1 for x > 0 and
+    e^x for x <= 0 (elu(x) = e^x - 1 there)."""
+    q = np.array([[[[0.5, -1.0]]]])
+    k = np.array([[[[2.0, -0.25]]]])
+    v = np.array([[[[3.0, -1.0, 0.5]]]])
+    s_raw = 0.5 * 2.0 + (-1.0) * (-0.25)
+    _close(orc.linear_attn(q, k, v, False)[0, 0, 0], s_raw * v[0, 0, 0], 1e-15, "raw row 0")
+    s = (0.5 + 1.0) * (2.0 + 1.0) + math.exp(-1.0) * math.exp(-0.25)
+    _close(orc.linear_attn(q, k, v, True, 1e-6)[0, 0, 0], s * v[0, 0, 0] / (s + 1e-6), 1e-15, "phi row 0")
+
+
+def pin_linear_constant_values(orc):
+    """Constant values c: every output row is c * S / (S + eps) with S = phi(q_j) . sum
+    phi(k_t) > 0, i.e. c up to eps; and eps = 0 gives c exactly (normalised weights)."""
+    rng = np.random.default_rng(63)
+    q, k = rng.standard_normal((2, 1, 2, 50, 8))
+    v = np.full((1, 2, 50, 5), 0.75)
+    _close(orc.linear_attn(q, k, v, True, 0.0), v, 1e-14, "constant values, eps 0")
+    out = orc.linear_attn(q, k, v, True, 1e-6)
+    assert np.all(out <= 0.75) and np.all(out > 0.75 * (1 - 1e-4)), "constant values, eps 1e-6"
+
+
+def pin_linear_causal_prefix(orc):
+    """Row j depends on tokens 0..j only: truncating the sequence after row j, or
+    changing later tokens, leaves rows 0..j unchanged (bit for bit)."""
+    rng = np.random.default_rng(64)
+    q, k = rng.standard_normal((2, 1, 1, 30, 6))
+    v = rng.standard_normal((1, 1, 30, 4))
+    full = orc.linear_attn(q, k, v, True)
+    pre = orc.linear_attn(q[:, :, :12], k[:, :, :12], v[:, :, :12], True)
+    assert np.array_equal(full[:, :, :12], pre), "causal prefix"
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 12:] += 5.0
+    v2[:, :, 12:] -= 3.0
+    assert np.array_equal(orc.linear_attn(q, k2, v2, True)[:, :, :12], full[:, :, :12]), "later tokens"
+    assert np.max(np.abs(orc.linear_attn(q, k2, v2, True)[:, :, 12:] - full[:, :, 12:])) > 1e-3
+
+
+def pin_linear_brute_force_integers(orc):
+    """Small integer inputs: the raw product is exact in fp64 and equals a pure-Python
+    triple loop bit for bit."""
+    rng = np.random.default_rng(65)
+    q = rng.integers(-3, 4, (1, 2, 7, 3)).astype(np.float64)
+    k = rng.integers(-3, 4, (1, 2, 7, 3)).astype(np.float64)
+    v = rng.integers(-3, 4, (1, 2, 7, 2)).astype(np.float64)
+    out = orc.linear_attn(q, k, v, False)
+    for h in range(2):
+        for j in range(7):
+            for m in range(2):
+                want = sum(sum(q[0, h, j, e] * k[0, h, t, e] for e in range(3)) * v[0, h, t, m]
+                           for t in range(j + 1))
+                assert out[0, h, j, m] == want, f"integer brute force h={h} j={j} m={m}"
+
+
+def pin_linear_heads_independent(orc):
+    """Each (batch, head) is its own sequence: computing one head alone gives its rows."""
+    rng = np.random.default_rng(66)
+    q, k = rng.standard_normal((2, 2, 3, 9, 4))
+    v = rng.standard_normal((2, 3, 9, 5))
+    full = orc.linear_attn(q, k, v, True)
+    for (b, h) in [(0, 0), (1, 2), (0, 1)]:
+        one = orc.linear_attn(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], True)
+        assert np.array_equal(one[0, 0], full[b, h]), f"head {b},{h}"
+
+
+def pin_linear_linear_in_values(orc):
+    """The output is linear in V: out(a V1 + V2) = a out(V1) + out(V2)."""
+    rng = np.random.default_rng(67)
+    q, k = rng.standard_normal((2, 1, 1, 20, 6))
+    v1, v2 = rng.standard_normal((2, 1, 1, 20, 3))
+    lhs = orc.linear_attn(q, k, 2.5 * v1 + v2, True)
+    rhs = 2.5 * orc.linear_attn(q, k, v1, True) + orc.linear_attn(q, k, v2, True)
+    _close(lhs, rhs, 1e-12, "linear in V")
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -57,6 +57,16 @@ MUTANTS = [
     ("masked_wrong_value_row", "o_i[c] += w * vh[j * d + c];", "o_i[c] += w * vh[c];"),
     ("masked_not_normalised", "const double w = s[j] / l;", "const double w = s[j];"),
     ("masked_diagonal_hidden", "if (causal && j > i + (Nk - Nq))", "if (causal && j >= i + (Nk - Nq))"),
+    ("lin_not_causal", "for (int64_t t = 0; t <= j; ++t) {   /* causal: keys t <= j */",
+     "for (int64_t t = 0; t < N; ++t) {   /* causal: keys t <= j */"),
+    ("lin_strictly_causal", "for (int64_t t = 0; t <= j; ++t) {   /* causal: keys t <= j */",
+     "for (int64_t t = 0; t < j + (j == 0); ++t) {   /* causal: keys t <= j */"),
+    ("lin_elu_without_one", "return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x) - 1.0;"),
+    ("lin_eps_dropped", "const double z = 1.0 / (den + eps);", "const double z = 1.0 / den;"),
+    ("lin_value_row_of_query", "const double *vt = v + (h * N + t) * M;", "const double *vt = v + (h * N + j) * M;"),
+    ("lin_denominator_unmapped", "for (int64_t e = 0; e < E; ++e) den += qj[e] * ksum[e];",
+     "for (int64_t e = 0; e < E; ++e) den += q[r * E + e] * ksum[e];"),
+    ("lin_feature_map_on_q_only", "fk[x] = feature_map ? elu_plus_one(k[x]) : k[x];", "fk[x] = k[x];"),
     ("bwd_scores_unscaled", "P[j] = dot * scale;\n                    if (P[j] > m) m = P[j];",
      "P[j] = dot;\n                    if (P[j] > m) m = P[j];"),
 ]
