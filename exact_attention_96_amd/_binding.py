@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_float, ci, ci, vp]
         L.attn_fwd_masked.restype = ci
         L.attn_mask_pack.argtypes = [vp, vp, vp, ll, ci, ci, vp]
+        L.attn_linear_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, vp]
+        L.attn_linear_fwd.restype = ci
         L.attn_mask_pack.restype = ci
         L.attn_strerror.argtypes = [ci]
         L.attn_strerror.restype = ctypes.c_char_p
@@ -86,6 +88,46 @@ def attn_mask_pack_ptr(mask: int, bits: int, tiles: int | None, heads: int, Nq: 
                        stream: int) -> int:
     """Raw call with integer device addresses (tiles None or 0: no summary)."""
     return int(lib().attn_mask_pack(mask, bits, tiles or None, heads, Nq, Nk, stream))
+
+
+def attn_linear_fwd_ptr(q: int, k: int, v: int, o: int, B: int, H: int, N: int, E: int, M: int,
+                        feature_map: int, eps: float, stream: int) -> int:
+    """Raw call with integer device addresses; returns the status code."""
+    return int(lib().attn_linear_fwd(q, k, v, o, B, H, N, E, M, feature_map, ctypes.c_float(eps), stream))
+
+
+def attn_linear_fwd(q, k, v, feature_map: bool = True, eps: float = 1e-6, out=None):
+    """Causal linear attention forward on the GPU (fp32).
+
+    q, k: [B, H, N, E]; v: [B, H, N, M]; float32, contiguous, one HIP device.
+    feature_map=True: phi = elu + 1 on q and k and the normaliser 1 / (phi(q_j) .
+    sum_{t<=j} phi(k_t) + eps); False: the causal dot product of q and k as given.
+    Returns o [B, H, N, M] float32, enqueued on torch's current stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's HIP device")
+        if not t.is_contiguous() or t.dtype != torch.float32 or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d float32 tensor")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"q, k [B, H, N, E] and v [B, H, N, M] expected, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    B, H, N, E = q.shape
+    M = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    if out.shape != v.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor like v")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_linear_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, E, M,
+                                 int(bool(feature_map)), float(eps), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, strerror(st), "attn_linear_fwd")
+    return out
 
 
 def attn_bwd_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,

@@ -10,6 +10,7 @@
 #include "fwd_f32.hpp"
 #include "bwd_mfma.hpp"
 #include "fwd_mfma.hpp"
+#include "linattn.hpp"
 
 namespace {
 
@@ -339,6 +340,49 @@ extern "C" ATTN_API int attn_bwd(const void *q, const void *k, const void *v, co
     const hipError_t err = d == 64 ? bwd_causal<64>(a, bh, causal, dtype, stream)
                                    : bwd_causal<128>(a, bh, causal, dtype, stream);
     return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+template <int E>
+hipError_t launch_linear(const attn::LinArgs &a, int grid, hipStream_t stream) {
+    typedef attn::LinFwd<E> K;
+    const hipError_t e = opt_in_lds<K>(reinterpret_cast<const void *>(&attn::attn_linear_fwd_kernel<E>), K::LDS_B);
+    if (e != hipSuccess) return e;
+    return launch(&attn::attn_linear_fwd_kernel<E>, grid, K::THREADS, K::LDS_B, stream, a);
+}
+
+extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, float *o, int B, int H, int N,
+                                        int E, int M, int feature_map, float eps, hipStream_t stream) {
+    if (!q || !k || !v || !o) return ATTN_EINVAL;
+    if (B < 1 || H < 1 || N < 1 || E < 1 || M < 1) return ATTN_EINVAL;
+    if (feature_map != 0 && feature_map != 1) return ATTN_EINVAL;
+    if (!isfinite(eps) || eps < 0.f) return ATTN_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_EINVAL;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t qb = rows * (uint64_t)E * 4, vb = rows * (uint64_t)M * 4;
+    if (overlaps(o, vb, q, qb) || overlaps(o, vb, k, qb) || overlaps(o, vb, v, vb)) return ATTN_EINVAL;
+    if (E != 16 && E != 32 && E != 64 && E != 128) return ATTN_EUNSUPPORTED;
+    if (M % 16 != 0) return ATTN_EUNSUPPORTED;
+    const uint64_t grid = (uint64_t)B * (uint64_t)H * (uint64_t)(M / 16);
+    if (grid > (uint64_t)INT32_MAX || (uint64_t)N * (uint64_t)(E > M ? E : M) > (uint64_t)INT32_MAX)
+        return ATTN_EUNSUPPORTED;
+    attn::LinArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.N = N;
+    a.M = M;
+    a.n_mslices = M / 16;
+    a.eps = eps;
+    a.feature_map = feature_map;
+    hipError_t e;
+    switch (E) {
+        case 16: e = launch_linear<16>(a, (int)grid, stream); break;
+        case 32: e = launch_linear<32>(a, (int)grid, stream); break;
+        case 64: e = launch_linear<64>(a, (int)grid, stream); break;
+        default: e = launch_linear<128>(a, (int)grid, stream); break;
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
 extern "C" ATTN_API const char *attn_strerror(int status) {

@@ -50,7 +50,7 @@ typedef enum {
 } attn_status_t;
 
 /* Version of this ABI; bumped when entry points change or are added. */
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /*
  * attn_fwd — attention forward for B*H independent heads.
@@ -222,6 +222,42 @@ ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o
                       const float *lse, const void *dout, void *dq, void *dk, void *dv,
                       float *delta, int B, int H, int N, int d, float scale, int causal,
                       int dtype, hipStream_t stream);
+
+/*
+ * attn_linear_fwd — causal linear attention forward (fp32) for B*H independent
+ * heads, a second attention method next to the softmax one above.
+ *
+ * From the hqwc.cn notes on the fast-transformers linear attention kernels
+ * ("Transformers are RNNs"): the similarity exp(q.k / sqrt(D)) is replaced by
+ * phi(q) . phi(k) with phi(x) = elu(x) + 1 (section 0x0); the causal module
+ * returns causal_dot_product(phi(Q), phi(K), V) times
+ * 1 / (phi(q_j) . sum_{t<=j} phi(k_t) + eps) (section 0x1); the causal dot
+ * product is V'_j = sum_{t<=j} (q_j . k_t) v_t (section 0x2).
+ *
+ * Arguments
+ *   q, k     device pointers, [B, H, N, E] contiguous fp32; read only.
+ *   v        device pointer, [B, H, N, M] contiguous fp32; read only.
+ *   o        device pointer, [B, H, N, M] contiguous fp32; written:
+ *            feature_map = 0: o_j = sum_{t<=j} (q_j . k_t) v_t (the causal dot
+ *            product of q and k as given); feature_map = 1: the same product of
+ *            phi(q), phi(k) and v, divided by phi(q_j) . sum_{t<=j} phi(k_t) + eps.
+ *   B, H, N  batch, heads, sequence length, each >= 1.
+ *   E        query/key width: 16, 32, 64 or 128.
+ *   M        value width: a multiple of 16.
+ *   eps      finite, >= 0 (used with feature_map = 1; the page's default 1e-6).
+ *   stream   HIP stream the work is enqueued on.
+ *
+ * Arithmetic: fp32 throughout; the state sum_{t<=j} phi(k_t) v_t^T is carried in
+ * token order.  Results are bitwise reproducible from call to call.
+ * Ownership: as attn_fwd; o must not overlap q, k or v.
+ * Errors (synchronous, nothing launched): ATTN_EINVAL (NULL pointer, a size < 1,
+ * feature_map not 0/1, eps negative or not finite, a pointer not 16-byte aligned,
+ * o overlapping an input), ATTN_EUNSUPPORTED (E not 16/32/64/128, M not a
+ * multiple of 16, a grid or row offset beyond 32 bits), ATTN_EHIP (launch).
+ */
+ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, float *o, int B,
+                             int H, int N, int E, int M, int feature_map, float eps,
+                             hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 ATTN_API const char *attn_strerror(int status);

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_fwd_masked",
-                                  "attn_mask_pack", "attn_strerror"]
+                                  "attn_linear_fwd", "attn_mask_pack", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -187,3 +187,28 @@ def test_masked_lse_right_after_mask_is_fine_to_check():
 ])
 def test_mask_pack_invalid_arguments(args):
     assert ea.attn_mask_pack_ptr(*args, 0) == ea.ATTN_EINVAL
+
+
+# attn_linear_fwd: host checks only (fake addresses, nothing launched).
+GOOD_L = dict(q=Q, k=K, v=V, o=O, B=2, H=3, N=100, E=64, M=64, fm=1, eps=1e-6, stream=0)
+L_ORDER = ["q", "k", "v", "o", "B", "H", "N", "E", "M", "fm", "eps", "stream"]
+
+
+def call_l(**kw):
+    a = dict(GOOD_L)
+    a.update(kw)
+    return ea.attn_linear_fwd_ptr(*(a[n] for n in L_ORDER))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(B=0), dict(H=-1), dict(N=0), dict(E=0), dict(M=0),
+    dict(fm=2), dict(eps=-1e-6), dict(eps=float("nan")), dict(q=Q + 4), dict(v=V + 8), dict(o=O + 12),
+    dict(o=Q), dict(o=K + 64), dict(o=V - 16),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_linear_invalid_arguments(kw):
+    assert call_l(**kw) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(E=48), dict(E=256), dict(M=40), dict(M=8)])
+def test_linear_unsupported(kw):
+    assert call_l(**kw) == ea.ATTN_EUNSUPPORTED

@@ -1,0 +1,134 @@
+"""GPU parity of attn_linear_fwd (causal linear attention, fp32) against the fp64
+oracle (oracle.linear_attn), through the C ABI.
+
+Bar (written here; a first-order rounding bound of the GPU's evaluation order,
+u = 2^-24).  The kernel carries the state S_j = sum_{t<=j} k_t v_t^T in fp32 in token
+order (j + 1 rounded additions) and reads out q_j . S_j with at most E more, so for the
+causal dot product
+    |o - o*|_jm <= (j + E + 2) u A_jm,   A_jm = sum_e |q_je| sum_{t<=j} |k_te| |v_tm|
+(A from the oracle on |q|, |k|, |v|).  With the feature map, phi(q), phi(k) carry at
+most 2 u of their own (expf within 2 ulp, x + 1 one rounding), the denominator is a sum
+of positive terms (relative error <= (j + E + 6) u) and the division adds u:
+    |o - o*|_jm <= (j + E + 8) u (A_jm / den_j + |o*_jm|),
+A and den from the oracle on phi(q), phi(k) (phi evaluated in fp64 here).
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_96_amd as ea
+import oracle
+from parity_util import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need an MI355X"
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+
+
+def inputs(B, H, N, E, M, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, N, E), generator=g) * std
+    k = torch.randn((B, H, N, E), generator=g) * std
+    v = torch.randn((B, H, N, M), generator=g)
+    return q, k, v
+
+
+def phi64(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def bound(q, k, v, fm, eps, o_ref):
+    N, E = q.shape[2], q.shape[3]
+    j = np.arange(N, dtype=np.float64).reshape(1, 1, N, 1)
+    if not fm:
+        A = oracle.linear_attn(np.abs(q.double().numpy()), np.abs(k.double().numpy()),
+                               np.abs(v.double().numpy()), False)
+        return (j + E + 2) * U * A
+    fq, fk = phi64(q), phi64(k)
+    A = oracle.linear_attn(fq, fk, np.abs(v.double().numpy()), False)
+    den = np.einsum("bhne,bhne->bhn", fq, np.cumsum(fk, axis=2))[..., None] + eps
+    return (j + E + 8) * U * (A / den + np.abs(o_ref))
+
+
+def check(q, k, v, fm, eps, what):
+    say(f"[linear] {what}: q={tuple(q.shape)} v={tuple(v.shape)} feature_map={fm}")
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=fm, eps=eps)
+    torch.cuda.synchronize()
+    o = o.cpu().double().numpy()
+    o_ref = oracle.linear_attn(q, k, v, fm, eps)
+    err = np.abs(o - o_ref)
+    bar = bound(q, k, v, fm, eps, o_ref)
+    ratio = float((err / bar).max())
+    say(f"[linear]   max err {err.max():.3e}, max err / bound {ratio:.4f}")
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    assert ratio <= 1.0, f"{what}: error {ratio:.3f} x the bound"
+    return o, o_ref, err
+
+
+SHAPES = [(1, 1, 1, 16, 16), (1, 2, 31, 32, 16), (2, 2, 100, 64, 64), (1, 3, 257, 128, 32),
+          (2, 1, 1000, 64, 48), (1, 1, 33, 16, 128), (1, 2, 700, 128, 64)]
+
+
+@pytest.mark.parametrize("fm", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape, fm):
+    q, k, v = inputs(*shape, seed=sum(shape))
+    check(q, k, v, fm, 1e-6, f"shape {shape}")
+
+
+def test_normalised_output_accuracy():
+    """With the feature map the output is a weighted mean of values: at N = 2048 its
+    error stays within the fp32 bar used for softmax attention (1e-5)."""
+    q, k, v = inputs(1, 2, 2048, 64, 64, seed=7)
+    _, _, err = check(q, k, v, True, 1e-6, "N 2048 normalised")
+    assert err.max() <= 1e-5
+
+
+def test_wide_inputs():
+    """Queries and keys scaled by 4: phi's exponential branch reaches e^-16 and its linear
+    branch 17, so the weights span ~10 decades."""
+    q, k, v = inputs(1, 2, 300, 64, 32, seed=8, std=4.0)
+    check(q, k, v, True, 1e-6, "wide inputs")
+
+
+def test_constant_values_and_zero_queries():
+    q, k, v = inputs(1, 1, 500, 32, 16, seed=9)
+    v = torch.full_like(v, -1.25)
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=True, eps=0.0).cpu()
+    assert torch.allclose(o, v, atol=2e-6, rtol=0)  # normalised weights of a constant
+    o = ea.attn_linear_fwd(torch.zeros_like(q).to(DEV), k.to(DEV), v.to(DEV), feature_map=False).cpu()
+    assert torch.equal(o, torch.zeros_like(o))       # q = 0: the product is exactly 0
+
+
+def test_causal_prefix_and_determinism():
+    q, k, v = inputs(2, 2, 600, 64, 32, seed=10)
+    a = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    b = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    assert torch.equal(a, b)
+    pre = ea.attn_linear_fwd(q[:, :, :250].contiguous().to(DEV), k[:, :, :250].contiguous().to(DEV),
+                             v[:, :, :250].contiguous().to(DEV)).cpu()
+    assert torch.equal(pre, a[:, :, :250])
+
+
+def test_full_size_workload():
+    """The benchmark shape (2 x 32 x 8192, E = M = 64, feature map): two heads in full
+    against the oracle, in the benchmark's launch."""
+    B, H, N, E, M = 2, 32, 8192, 64, 64
+    q, k, v = inputs(B, H, N, E, M, seed=11)
+    say(f"[linear] full size {(B, H, N, E, M)}")
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    assert torch.isfinite(o).all()
+    for (b, h) in [(0, 0), (1, 31)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref = oracle.linear_attn(q[sl], k[sl], v[sl], True, 1e-6)
+        err = np.abs(o[sl].double().numpy() - o_ref)
+        bar = bound(q[sl], k[sl], v[sl], True, 1e-6, o_ref)
+        say(f"[linear]   head ({b},{h}): max err {err.max():.3e}, max err / bound {(err / bar).max():.4f}")
+        assert (err / bar).max() <= 1.0
