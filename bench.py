@@ -17,6 +17,10 @@ forward's flops (five N x N x d products instead of two).
 With --workload m1|m2|m3 a step is one call of attn_fwd_masked (unequal query and
 key lengths, a boolean mask packed once before timing), counted at 4*d flops per
 visible (query, key) pair.
+
+With --workload l1 a step is one call of attn_linear_fwd (causal linear
+attention, fp32), a scan bound by HBM: the value is algorithmic GB/s (read q, k,
+v and write o once) against the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -205,7 +209,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3",
-                    help="c1..c5 (default: c3, the headline), or m1..m3 (masked / unequal lengths)")
+                    help="c1..c5 (default: c3, the headline), m1..m3 (masked / unequal lengths), "
+                         "or l1 (causal linear attention)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -235,10 +240,17 @@ def main():
 
     import torch
     import exact_attention_96_amd as ea
-    from exact_attention_96_amd.workloads import MASKED_WORKLOADS, WORKLOADS, make_inputs, random_grad
+    from exact_attention_96_amd.workloads import (LINEAR_WORKLOADS, MASKED_WORKLOADS, WORKLOADS, make_inputs,
+                                                  random_grad)
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    if args.workload in LINEAR_WORKLOADS:
+        if args.which != "fwd":
+            print("linear attention times the forward only", file=sys.stderr)
+            sys.exit(2)
+        bench_linear(args, LINEAR_WORKLOADS[args.workload])
         return
     if args.workload in MASKED_WORKLOADS:
         if args.which != "fwd":
@@ -329,6 +341,65 @@ def main():
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds) if bwd else
                                cpu_baseline(w, q, k, v, args.cpu_seconds))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_linear(lw, q, k, v, seconds: float):
+    """The fp64 oracle's causal linear attention on whole heads of the same workload,
+    head after head until `seconds` of wall time have been spent (at least one head)."""
+    import oracle
+    heads = [(b, h) for b in range(lw.B) for h in range(lw.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.linear_attn(q[sl], k[sl], v[sl], lw.feature_map, lw.eps)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = lw.io_bytes * done / (lw.B * lw.H)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {lw.B * lw.H} heads, all {lw.N} tokens each "
+                      f"({nbytes:.3e} algorithmic bytes in {dt:.1f} s; the oracle sums every "
+                      f"key of every row, O(N^2) per head)"}
+
+
+def bench_linear(args, lw):
+    import torch
+    import exact_attention_96_amd as ea
+    print(f"[bench] workload {lw.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = lw.inputs()
+    dev = "cuda:0"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(vd)
+
+    def step():
+        ea.attn_linear_fwd(qd, kd, vd, feature_map=lw.feature_map, eps=lw.eps, out=o)
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    wall, kernel_ms = time_steps(step, args.steps, args.warmup)
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    value = lw.io_bytes * args.steps / wall / 1e9
+    achieved = lw.io_bytes / avg_kernel_s / 1e9
+    out = {
+        "metric": "causal linear attention fwd: algorithmic HBM GB/s (fp32) and % of the 8 TB/s peak",
+        "value": round(value, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded randn inputs, see exact_attention_96_amd/workloads.py)",
+        "config": {"workload": lw.name, "B": lw.B, "H": lw.H, "N": lw.N, "E": lw.E, "M": lw.M,
+                   "feature_map": lw.feature_map, "eps": lw.eps},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": lw.io_bytes, "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
+                     "fp32_tflops": round(lw.flops / avg_kernel_s / 1e12, 2),
+                     "kernel_source_sha": kernel_source_hash()},
+    }
+    if args.cpu_seconds > 0 and args.cpu_heads != 0:
+        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_linear(lw, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -215,3 +215,42 @@ MASKED_WORKLOADS = {
     "m3": MaskedWorkload("m3_bf16_causal_nq2048_nk8192_b2h32d128", 2, 32, 2048, 8192, 128, "bf16",
                          True, seed=103),
 }
+
+
+@dataclass(frozen=True)
+class LinearWorkload:
+    """A workload of attn_linear_fwd (causal linear attention, fp32): q, k [B, H, N, E]
+    and v [B, H, N, M] drawn in that order as randn from one seeded generator."""
+    name: str
+    B: int
+    H: int
+    N: int
+    E: int
+    M: int
+    feature_map: bool = True
+    eps: float = 1e-6
+    seed: int = 0
+
+    @property
+    def io_bytes(self) -> int:
+        """Read q, k, v once and write o once (fp32)."""
+        return 4 * self.B * self.H * self.N * (2 * self.E + 2 * self.M)
+
+    @property
+    def flops(self) -> float:
+        """Per token: state update and readout, 2 E M each; key sum and denominator, 3 E."""
+        return float(self.B * self.H * self.N) * (4.0 * self.E * self.M + 3.0 * self.E)
+
+    def inputs(self):
+        g = torch.Generator(device="cpu")
+        g.manual_seed(self.seed)
+        q = torch.randn((self.B, self.H, self.N, self.E), generator=g)
+        k = torch.randn((self.B, self.H, self.N, self.E), generator=g)
+        v = torch.randn((self.B, self.H, self.N, self.M), generator=g)
+        return q, k, v
+
+
+# Causal linear attention at the headline sequence shape (B=2, H=32, N=8192), E = M = 64.
+LINEAR_WORKLOADS = {
+    "l1": LinearWorkload("l1_f32_causal_linear_b2h32n8192e64m64", 2, 32, 8192, 64, 64, seed=201),
+}
