@@ -8,10 +8,10 @@ from ._binding import (ATTN_BF16, ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATT
                        ATTN_F32, ATTN_OK, AttnError, abi_version, attn_bwd, attn_bwd_ptr,
                        attn_fwd, attn_fwd_masked, attn_fwd_masked_ptr, attn_fwd_ptr,
                        attn_mask_pack_ptr, pack_mask, PackedMask, strerror,
-                       attn_linear_fwd, attn_linear_fwd_ptr)
+                       attn_linear_fwd, attn_linear_fwd_ptr, linear_workspace_bytes)
 
 __all__ = ["attn_fwd", "attn_fwd_ptr", "attn_fwd_masked", "attn_fwd_masked_ptr", "pack_mask", "PackedMask",
-           "attn_linear_fwd", "attn_linear_fwd_ptr",
+           "attn_linear_fwd", "attn_linear_fwd_ptr", "linear_workspace_bytes",
            "attn_mask_pack_ptr", "attn_bwd", "attn_bwd_ptr", "abi_version", "strerror",
            "AttnError", "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_EHIP"]

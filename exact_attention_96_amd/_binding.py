@@ -48,8 +48,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_float, ci, ci, vp]
         L.attn_fwd_masked.restype = ci
         L.attn_mask_pack.argtypes = [vp, vp, vp, ll, ci, ci, vp]
-        L.attn_linear_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, vp]
+        L.attn_linear_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, vp, ll, vp]
         L.attn_linear_fwd.restype = ci
+        L.attn_linear_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+        L.attn_linear_workspace_bytes.restype = ll
         L.attn_mask_pack.restype = ci
         L.attn_strerror.argtypes = [ci]
         L.attn_strerror.restype = ctypes.c_char_p
@@ -91,17 +93,26 @@ def attn_mask_pack_ptr(mask: int, bits: int, tiles: int | None, heads: int, Nq: 
 
 
 def attn_linear_fwd_ptr(q: int, k: int, v: int, o: int, B: int, H: int, N: int, E: int, M: int,
-                        feature_map: int, eps: float, stream: int) -> int:
+                        feature_map: int, eps: float, stream: int, workspace: int | None = None,
+                        workspace_bytes: int = 0) -> int:
     """Raw call with integer device addresses; returns the status code."""
-    return int(lib().attn_linear_fwd(q, k, v, o, B, H, N, E, M, feature_map, ctypes.c_float(eps), stream))
+    return int(lib().attn_linear_fwd(q, k, v, o, B, H, N, E, M, feature_map, ctypes.c_float(eps),
+                                     workspace or None, workspace_bytes, stream))
 
 
-def attn_linear_fwd(q, k, v, feature_map: bool = True, eps: float = 1e-6, out=None):
+def linear_workspace_bytes(B: int, H: int, N: int, E: int, M: int) -> int:
+    return int(lib().attn_linear_workspace_bytes(B, H, N, E, M))
+
+
+def attn_linear_fwd(q, k, v, feature_map: bool = True, eps: float = 1e-6, out=None, chunked: bool = True,
+                    workspace=None):
     """Causal linear attention forward on the GPU (fp32).
 
     q, k: [B, H, N, E]; v: [B, H, N, M]; float32, contiguous, one HIP device.
     feature_map=True: phi = elu + 1 on q and k and the normaliser 1 / (phi(q_j) .
     sum_{t<=j} phi(k_t) + eps); False: the causal dot product of q and k as given.
+    chunked=True runs the chunked form on a workspace (allocated here with torch unless
+    one is passed: a uint8 tensor of at least linear_workspace_bytes); False the scan.
     Returns o [B, H, N, M] float32, enqueued on torch's current stream.
     """
     import torch
@@ -121,10 +132,19 @@ def attn_linear_fwd(q, k, v, feature_map: bool = True, eps: float = 1e-6, out=No
         out = torch.empty_like(v)
     if out.shape != v.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous float32 tensor like v")
+    ws_ptr, ws_bytes = None, 0
+    if chunked:
+        need = linear_workspace_bytes(B, H, N, E, M)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous() \
+                or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = attn_linear_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, E, M,
-                                 int(bool(feature_map)), float(eps), stream)
+                                 int(bool(feature_map)), float(eps), stream, ws_ptr, ws_bytes)
     if st != ATTN_OK:
         raise AttnError(st, strerror(st), "attn_linear_fwd")
     return out

@@ -350,8 +350,44 @@ hipError_t launch_linear(const attn::LinArgs &a, int grid, hipStream_t stream) {
     return launch(&attn::attn_linear_fwd_kernel<E>, grid, K::THREADS, K::LDS_B, stream, a);
 }
 
+template <int E>
+hipError_t launch_linear_chunked(const attn::LinChunkArgs &a, int bh, hipStream_t stream) {
+    typedef attn::LinChunk<E> K;
+    const int grid = bh * a.n_chunks;  // bounded by the checks in attn_linear_fwd
+    const int s_lds = K::states_lds(a.M), o_lds = K::outputs_lds(a.M);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn::attn_linear_states_kernel<E>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, s_lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn::attn_linear_outputs_kernel<E>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, o_lds);
+    if (e != hipSuccess) return e;
+    e = launch(&attn::attn_linear_states_kernel<E>, grid, K::THREADS, s_lds, stream, a);
+    if (e != hipSuccess) return e;
+    const int per_chunk = E * a.M + E, bph = (per_chunk + 255) / 256;
+    e = launch(&attn::attn_linear_prefix_kernel, bh * bph, 256, 0, stream, a.ws, a.n_chunks, per_chunk, bph);
+    if (e != hipSuccess) return e;
+    return launch(&attn::attn_linear_outputs_kernel<E>, grid, K::THREADS, o_lds, stream, a);
+}
+
+// LDS of the chunked output kernel for (E, M); the chunked form is used only where it fits.
+int linear_chunk_lds(int E, int M) {
+    switch (E) {
+        case 16: return attn::LinChunk<16>::outputs_lds(M);
+        case 32: return attn::LinChunk<32>::outputs_lds(M);
+        case 64: return attn::LinChunk<64>::outputs_lds(M);
+        default: return attn::LinChunk<128>::outputs_lds(M);
+    }
+}
+
+extern "C" ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M) {
+    if (B < 1 || H < 1 || N < 1 || E < 1 || M < 1) return -1;
+    const uint64_t chunks = ((uint64_t)N + attn::LinChunk<16>::TC - 1) / attn::LinChunk<16>::TC;
+    return (long long)((uint64_t)B * (uint64_t)H * chunks * ((uint64_t)E * (uint64_t)M + (uint64_t)E) * 4);
+}
+
 extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, float *o, int B, int H, int N,
-                                        int E, int M, int feature_map, float eps, hipStream_t stream) {
+                                        int E, int M, int feature_map, float eps, void *workspace,
+                                        long long workspace_bytes, hipStream_t stream) {
     if (!q || !k || !v || !o) return ATTN_EINVAL;
     if (B < 1 || H < 1 || N < 1 || E < 1 || M < 1) return ATTN_EINVAL;
     if (feature_map != 0 && feature_map != 1) return ATTN_EINVAL;
@@ -360,11 +396,43 @@ extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const fl
     const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
     const uint64_t qb = rows * (uint64_t)E * 4, vb = rows * (uint64_t)M * 4;
     if (overlaps(o, vb, q, qb) || overlaps(o, vb, k, qb) || overlaps(o, vb, v, vb)) return ATTN_EINVAL;
+    const long long need = attn_linear_workspace_bytes(B, H, N, E, M);
+    if (workspace) {
+        if (!aligned(workspace, 16) || workspace_bytes < need) return ATTN_EINVAL;
+        const void *outs[] = {q, k, v, o};
+        const uint64_t ob[] = {qb, qb, vb, vb};
+        for (int i = 0; i < 4; ++i)
+            if (overlaps(workspace, (uint64_t)need, outs[i], ob[i])) return ATTN_EINVAL;
+    }
     if (E != 16 && E != 32 && E != 64 && E != 128) return ATTN_EUNSUPPORTED;
     if (M % 16 != 0) return ATTN_EUNSUPPORTED;
     const uint64_t grid = (uint64_t)B * (uint64_t)H * (uint64_t)(M / 16);
     if (grid > (uint64_t)INT32_MAX || (uint64_t)N * (uint64_t)(E > M ? E : M) > (uint64_t)INT32_MAX)
         return ATTN_EUNSUPPORTED;
+    const uint64_t chunks = ((uint64_t)N + 63) / 64;
+    if (workspace && linear_chunk_lds(E, M) <= 160 * 1024 && (uint64_t)B * (uint64_t)H * chunks <= (uint64_t)INT32_MAX &&
+        (uint64_t)B * (uint64_t)H * (((uint64_t)E * M + E + 255) / 256) <= (uint64_t)INT32_MAX) {
+        attn::LinChunkArgs c;
+        c.q = q;
+        c.k = k;
+        c.v = v;
+        c.o = o;
+        c.ws = static_cast<float *>(workspace);
+        c.N = N;
+        c.M = M;
+        c.n_chunks = (int)chunks;
+        c.eps = eps;
+        c.feature_map = feature_map;
+        const int bh = B * H;
+        hipError_t e;
+        switch (E) {
+            case 16: e = launch_linear_chunked<16>(c, bh, stream); break;
+            case 32: e = launch_linear_chunked<32>(c, bh, stream); break;
+            case 64: e = launch_linear_chunked<64>(c, bh, stream); break;
+            default: e = launch_linear_chunked<128>(c, bh, stream); break;
+        }
+        return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+    }
     attn::LinArgs a;
     a.q = q;
     a.k = k;

@@ -179,3 +179,289 @@ __global__ __launch_bounds__(256) void attn_linear_fwd_kernel(LinArgs a) {
 }
 
 }  // namespace attn
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// Chunked form of the same computation, for a caller's workspace.  The page's
+// sum over t <= j splits at chunk boundaries (chunks of TC tokens):
+//   o_j = phi(q_j) S_c + sum_{t in chunk c, t <= j} (phi(q_j) . phi(k_t)) v_t,
+//   S_c = sum over earlier chunks of phi(K)^T V,
+// and likewise the normaliser with z_c = sum over earlier chunks of phi(k_t).
+// Three launches: (1) per chunk, its own phi(K_c)^T V_c and key sum into the
+// workspace; (2) per head, an exclusive prefix of those over the chunks, in place;
+// (3) per chunk, the outputs.  Every launch has B * H * (chunks) or more
+// workgroups, instead of one sequential scan per (head, column slice).
+// Workspace: [B * H][n_chunks][E * M + E] fp32 (state, then key sum).
+
+struct LinChunkArgs {
+    const float *q, *k, *v;
+    float *o;
+    float *ws;
+    int N, M, n_chunks;
+    float eps;
+    int feature_map;
+};
+
+template <int E>
+struct LinChunk {
+    static constexpr int TC = 64;          // tokens per chunk
+    static constexpr int TP = TC + 4;      // row stride of the transposed LDS tiles: a wave's
+                                           // transposing writes spread over 16 banks instead of
+                                           // one, and rows stay 16-byte aligned for the reads
+    static constexpr int THREADS = 256;
+    static __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+    // chunk rows [c0, c0 + TC) of a [N, W] tensor into LDS transposed, dst[w * TP + t]
+    // (zeros past the end; the feature map if fm).  Each thread issues all its 16-byte
+    // loads before the first use, so the chunk costs one memory latency, not one per load.
+    template <int W>
+    static __device__ __forceinline__ void load_t(float *dst, const float *src, int c0, int N, bool fm) {
+        constexpr int PER = TC * W / 4 / THREADS;
+        static_assert(PER >= 1 && PER * THREADS * 4 == TC * W, "whole 16-byte pieces per thread");
+        f32x4_t val[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int x = threadIdx.x + j * THREADS, t = x / (W / 4), c4 = x - t * (W / 4);
+            val[j] = c0 + t < N ? *reinterpret_cast<const f32x4_t *>(src + (size_t)(c0 + t) * W + 4 * c4)
+                                : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int x = threadIdx.x + j * THREADS, t = x / (W / 4), c4 = x - t * (W / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(4 * c4 + i) * TP + t] = fm && c0 + t < N ? phi(val[j][i]) : val[j][i];
+        }
+    }
+    // the same for a width known only at run time (v in the state kernel), four loads at a time
+    static __device__ __forceinline__ void load_t_rt(float *dst, const float *src, int c0, int N, int W) {
+        const int n4 = TC * W / 4;
+        for (int x0 = threadIdx.x; x0 < n4; x0 += 4 * THREADS) {
+            f32x4_t val[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int x = x0 + j * THREADS, t = x / (W / 4), c4 = x - t * (W / 4);
+                val[j] = x < n4 && c0 + t < N ? *reinterpret_cast<const f32x4_t *>(src + (size_t)(c0 + t) * W + 4 * c4)
+                                              : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int x = x0 + j * THREADS, t = x / (W / 4), c4 = x - t * (W / 4);
+                if (x < n4)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[(4 * c4 + i) * TP + t] = val[j][i];
+            }
+        }
+    }
+
+    // (1) per (head, chunk): dS = phi(K_c)^T V_c [E][M] and dz = sum_t phi(k_t) [E]
+    static __device__ void states(const LinChunkArgs &a) {
+        extern __shared__ __attribute__((aligned(16))) float lds[];
+        const int N = a.N, M = a.M;
+        const int bh = blockIdx.x / a.n_chunks, c = blockIdx.x - bh * a.n_chunks, c0 = c * TC;
+        float *Kt = lds;            // [E][TP]
+        float *Vt = lds + E * TP;   // [M][TP]
+        load_t<E>(Kt, a.k + (size_t)bh * N * E, c0, N, a.feature_map != 0);
+        load_t_rt(Vt, a.v + (size_t)bh * N * M, c0, N, M);
+        __syncthreads();
+        float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
+        // 4 x 4 blocks of (e, m)
+        const int nb = (E / 4) * (M / 4);
+        for (int blk = threadIdx.x; blk < nb; blk += THREADS) {
+            const int e0 = 4 * (blk / (M / 4)), m0 = 4 * (blk % (M / 4));
+            float acc[4][4] = {};
+#pragma unroll 2
+            for (int t = 0; t < TC; t += 4) {
+                f32x4_t kk[4], vv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kk[i] = *reinterpret_cast<const f32x4_t *>(Kt + (e0 + i) * TP + t);
+                    vv[i] = *reinterpret_cast<const f32x4_t *>(Vt + (m0 + i) * TP + t);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(kk[i][tt], vv[j][tt], acc[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4_t *>(W + (size_t)(e0 + i) * M + m0) =
+                    (f32x4_t){acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+        }
+        for (int e = threadIdx.x; e < E; e += THREADS) {
+            float zz = 0.f;
+            for (int t = 0; t < TC; ++t) zz += Kt[e * TP + t];
+            W[(size_t)E * M + e] = zz;
+        }
+    }
+
+    // (3) per (head, chunk): outputs of the chunk's rows from the prefix S_c, z_c (workspace)
+    static __device__ void outputs(const LinChunkArgs &a) {
+        extern __shared__ __attribute__((aligned(16))) float lds[];
+        const int N = a.N, M = a.M;
+        const bool fm = a.feature_map != 0;
+        const int bh = blockIdx.x / a.n_chunks, c = blockIdx.x - bh * a.n_chunks, c0 = c * TC;
+        constexpr int KA = E * TP > TC * TC ? E * TP : TC * TC;  // K^T, later A^T
+        float *Qt = lds;               // [E][TP]
+        float *Kt = Qt + E * TP;       // [E][TP]
+        float *Vr = Kt + KA;           // [TC][M] (row-major)
+        float *Sc = Vr + TC * M;       // [E][M] + z [E]
+        float *At = Kt;                // [TC (key t')][TC (query t)]: A^T, causal; written over
+                                       // K^T (region of KA floats) once every block of A is in registers
+        float *Dn = Sc + E * M + E;    // [TC] denominators
+        load_t<E>(Qt, a.q + (size_t)bh * N * E, c0, N, fm);
+        load_t<E>(Kt, a.k + (size_t)bh * N * E, c0, N, fm);
+        {
+            const float *src = a.v + (size_t)bh * N * M;
+#pragma unroll 4
+            for (int x = threadIdx.x; x < TC * M / 4; x += THREADS) {
+                const int t = x / (M / 4), c4 = x - t * (M / 4);
+                f32x4_t val = {0.f, 0.f, 0.f, 0.f};
+                if (c0 + t < N) val = *reinterpret_cast<const f32x4_t *>(src + (size_t)(c0 + t) * M + 4 * c4);
+                *reinterpret_cast<f32x4_t *>(Vr + t * M + 4 * c4) = val;
+            }
+            const float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
+#pragma unroll 4
+            for (int x = threadIdx.x; x < (E * M + E) / 4; x += THREADS)
+                *reinterpret_cast<f32x4_t *>(Sc + 4 * x) = *reinterpret_cast<const f32x4_t *>(W + 4 * x);
+        }
+        __syncthreads();
+        // A^T[t'][t] = phi(q_t) . phi(k_t') for t' <= t, else 0: 4 x 4 blocks (t', t), each
+        // thread's blocks in registers until every thread is done with K^T
+        constexpr int NB = (TC / 4) * (TC / 4), BPT = (NB + THREADS - 1) / THREADS;
+        float ablk[BPT][4][4];
+#pragma unroll
+        for (int r = 0; r < BPT; ++r) {
+            const int blk = threadIdx.x + r * THREADS;
+            const int p0 = 4 * (blk / (TC / 4)), t0 = 4 * (blk % (TC / 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ablk[r][i][j] = 0.f;
+            if (blk < NB && p0 <= t0 + 3) {
+#pragma unroll 8
+                for (int e = 0; e < E; ++e) {
+                    const f32x4_t kk = *reinterpret_cast<const f32x4_t *>(Kt + e * TP + p0);
+                    const f32x4_t qq = *reinterpret_cast<const f32x4_t *>(Qt + e * TP + t0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ablk[r][i][j] = fmaf(kk[i], qq[j], ablk[r][i][j]);
+                }
+            }
+        }
+        __syncthreads();  // K^T is read by every thread above; A^T takes its place
+#pragma unroll
+        for (int r = 0; r < BPT; ++r) {
+            const int blk = threadIdx.x + r * THREADS;
+            if (blk >= NB) break;
+            const int p0 = 4 * (blk / (TC / 4)), t0 = 4 * (blk % (TC / 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4_t row;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) row[j] = p0 + i <= t0 + j ? ablk[r][i][j] : 0.f;
+                *reinterpret_cast<f32x4_t *>(At + (p0 + i) * TC + t0) = row;
+            }
+        }
+        __syncthreads();
+        // denominators: phi(q_t) . z_c + sum_{t' <= t} A[t][t'], four rows per thread
+        if (fm && threadIdx.x < TC / 4) {
+            const int t0 = 4 * threadIdx.x;
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < E; ++e) {
+                const f32x4_t qq = *reinterpret_cast<const f32x4_t *>(Qt + e * TP + t0);
+                const float zz = Sc[E * M + e];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] = fmaf(qq[j], zz, d[j]);
+            }
+            for (int p = 0; p <= t0 + 3; ++p) {  // A^T is zero above each row's diagonal
+                const f32x4_t aa = *reinterpret_cast<const f32x4_t *>(At + p * TC + t0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] += aa[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Dn[t0 + j] = d[j] + a.eps;
+        }
+        __syncthreads();
+        // outputs: 4 x 4 blocks (t, m): phi(Q) S_c + A V
+        float *Oh = a.o + (size_t)bh * N * M;
+        for (int blk = threadIdx.x; blk < (TC / 4) * (M / 4); blk += THREADS) {
+            const int t0 = 4 * (blk / (M / 4)), m0 = 4 * (blk % (M / 4));
+            float acc[4][4] = {};
+#pragma unroll 8
+            for (int e = 0; e < E; ++e) {
+                const f32x4_t qq = *reinterpret_cast<const f32x4_t *>(Qt + e * TP + t0);
+                const f32x4_t ss = *reinterpret_cast<const f32x4_t *>(Sc + e * M + m0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(qq[i], ss[j], acc[i][j]);
+            }
+            // (several iterations' reads in flight: with one workgroup per CU nothing
+            // else hides the LDS latency)
+#pragma unroll 8
+            for (int p = 0; p <= t0 + 3; ++p) {  // keys of the chunk up to the block's last row
+                const f32x4_t aa = *reinterpret_cast<const f32x4_t *>(At + p * TC + t0);
+                const f32x4_t vv = *reinterpret_cast<const f32x4_t *>(Vr + p * M + m0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(aa[i], vv[j], acc[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (c0 + t0 + i >= N) break;
+                const float inv = fm ? 1.f / Dn[t0 + i] : 1.f;
+                *reinterpret_cast<f32x4_t *>(Oh + (size_t)(c0 + t0 + i) * M + m0) =
+                    (f32x4_t){acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv};
+            }
+        }
+    }
+
+    static constexpr int states_lds(int M) { return (E * TP + M * TP) * 4; }
+    static constexpr int outputs_lds(int M) {
+        return (E * TP + (E * TP > TC * TC ? E * TP : TC * TC) + TC * M + E * M + E + TC) * 4;
+    }
+};
+
+template <int E>
+__global__ __launch_bounds__(256) void attn_linear_states_kernel(LinChunkArgs a) {
+    LinChunk<E>::states(a);
+}
+
+template <int E>
+__global__ __launch_bounds__(256, 2) void attn_linear_outputs_kernel(LinChunkArgs a) {
+    LinChunk<E>::outputs(a);
+}
+
+// (2) exclusive prefix over the chunks of each head, in place: thread x of the head
+// owns workspace entry x of every chunk (state and key sum alike).
+__global__ __launch_bounds__(256) void attn_linear_prefix_kernel(float *ws, int n_chunks, int per_chunk,
+                                                                 int blocks_per_head) {
+    const int bh = blockIdx.x / blocks_per_head;
+    const int x = (blockIdx.x - bh * blocks_per_head) * 256 + threadIdx.x;
+    if (x >= per_chunk) return;
+    float *p = ws + (size_t)bh * n_chunks * per_chunk + x;
+    float run = 0.f;
+    int c = 0;
+    for (; c + 4 <= n_chunks; c += 4) {  // four loads in flight
+        float d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = p[(size_t)(c + i) * per_chunk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[(size_t)(c + i) * per_chunk] = run;
+            run += d[i];
+        }
+    }
+    for (; c < n_chunks; ++c) {
+        const float d = p[(size_t)c * per_chunk];
+        p[(size_t)c * per_chunk] = run;
+        run += d;
+    }
+}
+
+}  // namespace attn

@@ -50,7 +50,7 @@ typedef enum {
 } attn_status_t;
 
 /* Version of this ABI; bumped when entry points change or are added. */
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /*
  * attn_fwd — attention forward for B*H independent heads.
@@ -245,19 +245,35 @@ ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o
  *   E        query/key width: 16, 32, 64 or 128.
  *   M        value width: a multiple of 16.
  *   eps      finite, >= 0 (used with feature_map = 1; the page's default 1e-6).
+ *   workspace  NULL, or device memory of at least attn_linear_workspace_bytes(B,
+ *            H, N, E, M) bytes, 16-byte aligned, owned by the caller, overwritten
+ *            (it must not overlap q, k, v or o).  With it the sequence is split
+ *            into chunks of 64 tokens: per chunk phi(K)^T V and the key sum go to
+ *            the workspace, an exclusive prefix over the chunks follows, and each
+ *            chunk's outputs are phi(Q) times its prefix plus the causal
+ *            in-chunk product (three launches, parallel over chunks).  Without
+ *            it (or where the chunk tiles do not fit in LDS: E * M large) one
+ *            sequential scan per (head, 16 value columns) runs instead.
+ *   workspace_bytes  size of workspace in bytes (ignored when it is NULL).
  *   stream   HIP stream the work is enqueued on.
  *
- * Arithmetic: fp32 throughout; the state sum_{t<=j} phi(k_t) v_t^T is carried in
- * token order.  Results are bitwise reproducible from call to call.
+ * Arithmetic: fp32 throughout; the scan carries the state in token order, the
+ * chunked form sums per chunk then over chunks (results of the two forms differ by
+ * rounding).  Results of one form are bitwise reproducible from call to call.
  * Ownership: as attn_fwd; o must not overlap q, k or v.
  * Errors (synchronous, nothing launched): ATTN_EINVAL (NULL pointer, a size < 1,
  * feature_map not 0/1, eps negative or not finite, a pointer not 16-byte aligned,
- * o overlapping an input), ATTN_EUNSUPPORTED (E not 16/32/64/128, M not a
- * multiple of 16, a grid or row offset beyond 32 bits), ATTN_EHIP (launch).
+ * o overlapping an input, a workspace too small or overlapping a tensor),
+ * ATTN_EUNSUPPORTED (E not 16/32/64/128, M not a multiple of 16, a grid or row
+ * offset beyond 32 bits), ATTN_EHIP (launch).
  */
 ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, float *o, int B,
                              int H, int N, int E, int M, int feature_map, float eps,
-                             hipStream_t stream);
+                             void *workspace, long long workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attn_linear_fwd's chunked form needs for these sizes
+ * (B * H * ceil(N / 64) * (E * M + E) * 4), or -1 for a size < 1. */
+ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 ATTN_API const char *attn_strerror(int status);

@@ -20,7 +20,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_fwd_masked",
-                                  "attn_linear_fwd", "attn_mask_pack", "attn_strerror"]
+                                  "attn_linear_fwd", "attn_linear_workspace_bytes", "attn_mask_pack",
+                                  "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -190,8 +191,10 @@ def test_mask_pack_invalid_arguments(args):
 
 
 # attn_linear_fwd: host checks only (fake addresses, nothing launched).
-GOOD_L = dict(q=Q, k=K, v=V, o=O, B=2, H=3, N=100, E=64, M=64, fm=1, eps=1e-6, stream=0)
-L_ORDER = ["q", "k", "v", "o", "B", "H", "N", "E", "M", "fm", "eps", "stream"]
+WS = 13 << 40
+GOOD_L = dict(q=Q, k=K, v=V, o=O, B=2, H=3, N=100, E=64, M=64, fm=1, eps=1e-6, stream=0, ws=WS,
+              ws_bytes=2 * 3 * 2 * (64 * 64 + 64) * 4)
+L_ORDER = ["q", "k", "v", "o", "B", "H", "N", "E", "M", "fm", "eps", "stream", "ws", "ws_bytes"]
 
 
 def call_l(**kw):
@@ -204,6 +207,7 @@ def call_l(**kw):
     dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(B=0), dict(H=-1), dict(N=0), dict(E=0), dict(M=0),
     dict(fm=2), dict(eps=-1e-6), dict(eps=float("nan")), dict(q=Q + 4), dict(v=V + 8), dict(o=O + 12),
     dict(o=Q), dict(o=K + 64), dict(o=V - 16),
+    dict(ws=WS + 8), dict(ws_bytes=1000), dict(ws=Q + 64), dict(ws=O - 256),
 ], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
 def test_linear_invalid_arguments(kw):
     assert call_l(**kw) == ea.ATTN_EINVAL
@@ -211,4 +215,10 @@ def test_linear_invalid_arguments(kw):
 
 @pytest.mark.parametrize("kw", [dict(E=48), dict(E=256), dict(M=40), dict(M=8)])
 def test_linear_unsupported(kw):
-    assert call_l(**kw) == ea.ATTN_EUNSUPPORTED
+    assert call_l(ws=0, **kw) == ea.ATTN_EUNSUPPORTED
+
+
+def test_linear_workspace_bytes():
+    assert ea.linear_workspace_bytes(2, 3, 100, 64, 64) == 2 * 3 * 2 * (64 * 64 + 64) * 4
+    assert ea.linear_workspace_bytes(1, 1, 64, 16, 16) == 1 * 1 * 1 * (16 * 16 + 16) * 4
+    assert ea.linear_workspace_bytes(0, 1, 64, 16, 16) == -1

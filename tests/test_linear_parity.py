@@ -11,6 +11,10 @@ most 2 u of their own (expf within 2 ulp, x + 1 one rounding), the denominator i
 of positive terms (relative error <= (j + E + 6) u) and the division adds u:
     |o - o*|_jm <= (j + E + 8) u (A_jm / den_j + |o*_jm|),
 A and den from the oracle on phi(q), phi(k) (phi evaluated in fp64 here).
+The chunked form (a workspace) sums a chunk of at most 64 tokens, then the chunk
+sums over the chunks, then adds the in-chunk products (a 64-term sum of E-term
+products), so it gets 2 * 64 more rounded additions in the same bound.
+Both forms run on every case.
 """
 import numpy as np
 import pytest
@@ -44,9 +48,9 @@ def phi64(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def bound(q, k, v, fm, eps, o_ref):
+def bound(q, k, v, fm, eps, o_ref, chunked):
     N, E = q.shape[2], q.shape[3]
-    j = np.arange(N, dtype=np.float64).reshape(1, 1, N, 1)
+    j = np.arange(N, dtype=np.float64).reshape(1, 1, N, 1) + (128 if chunked else 0)
     if not fm:
         A = oracle.linear_attn(np.abs(q.double().numpy()), np.abs(k.double().numpy()),
                                np.abs(v.double().numpy()), False)
@@ -57,14 +61,14 @@ def bound(q, k, v, fm, eps, o_ref):
     return (j + E + 8) * U * (A / den + np.abs(o_ref))
 
 
-def check(q, k, v, fm, eps, what):
-    say(f"[linear] {what}: q={tuple(q.shape)} v={tuple(v.shape)} feature_map={fm}")
-    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=fm, eps=eps)
+def check(q, k, v, fm, eps, what, chunked=True):
+    say(f"[linear] {what}: q={tuple(q.shape)} v={tuple(v.shape)} feature_map={fm} chunked={chunked}")
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=fm, eps=eps, chunked=chunked)
     torch.cuda.synchronize()
     o = o.cpu().double().numpy()
     o_ref = oracle.linear_attn(q, k, v, fm, eps)
     err = np.abs(o - o_ref)
-    bar = bound(q, k, v, fm, eps, o_ref)
+    bar = bound(q, k, v, fm, eps, o_ref, chunked)
     ratio = float((err / bar).max())
     say(f"[linear]   max err {err.max():.3e}, max err / bound {ratio:.4f}")
     assert np.isfinite(o).all(), f"{what}: non-finite output"
@@ -76,59 +80,72 @@ SHAPES = [(1, 1, 1, 16, 16), (1, 2, 31, 32, 16), (2, 2, 100, 64, 64), (1, 3, 257
           (2, 1, 1000, 64, 48), (1, 1, 33, 16, 128), (1, 2, 700, 128, 64)]
 
 
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
 @pytest.mark.parametrize("fm", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_shapes(shape, fm):
+def test_shapes(shape, fm, chunked):
     q, k, v = inputs(*shape, seed=sum(shape))
-    check(q, k, v, fm, 1e-6, f"shape {shape}")
+    check(q, k, v, fm, 1e-6, f"shape {shape}", chunked)
 
 
-def test_normalised_output_accuracy():
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
+def test_normalised_output_accuracy(chunked):
     """With the feature map the output is a weighted mean of values: at N = 2048 its
     error stays within the fp32 bar used for softmax attention (1e-5)."""
     q, k, v = inputs(1, 2, 2048, 64, 64, seed=7)
-    _, _, err = check(q, k, v, True, 1e-6, "N 2048 normalised")
+    _, _, err = check(q, k, v, True, 1e-6, "N 2048 normalised", chunked)
     assert err.max() <= 1e-5
 
 
-def test_wide_inputs():
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
+def test_wide_inputs(chunked):
     """Queries and keys scaled by 4: phi's exponential branch reaches e^-16 and its linear
     branch 17, so the weights span ~10 decades."""
     q, k, v = inputs(1, 2, 300, 64, 32, seed=8, std=4.0)
-    check(q, k, v, True, 1e-6, "wide inputs")
+    check(q, k, v, True, 1e-6, "wide inputs", chunked)
+
+
+def test_large_value_width_falls_back_to_the_scan():
+    """E = 128 with M = 256 does not fit the chunk tiles in LDS: the call with a
+    workspace runs the scan and meets the scan's bound."""
+    q, k, v = inputs(1, 1, 200, 128, 256, seed=12)
+    check(q, k, v, True, 1e-6, "E 128 M 256", True)
 
 
 def test_constant_values_and_zero_queries():
     q, k, v = inputs(1, 1, 500, 32, 16, seed=9)
     v = torch.full_like(v, -1.25)
-    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=True, eps=0.0).cpu()
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), feature_map=True, eps=0.0).cpu()  # chunked
     assert torch.allclose(o, v, atol=2e-6, rtol=0)  # normalised weights of a constant
     o = ea.attn_linear_fwd(torch.zeros_like(q).to(DEV), k.to(DEV), v.to(DEV), feature_map=False).cpu()
     assert torch.equal(o, torch.zeros_like(o))       # q = 0: the product is exactly 0
 
 
-def test_causal_prefix_and_determinism():
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
+def test_causal_prefix_and_determinism(chunked):
     q, k, v = inputs(2, 2, 600, 64, 32, seed=10)
-    a = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
-    b = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    a = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunked=chunked).cpu()
+    b = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunked=chunked).cpu()
     assert torch.equal(a, b)
-    pre = ea.attn_linear_fwd(q[:, :, :250].contiguous().to(DEV), k[:, :, :250].contiguous().to(DEV),
-                             v[:, :, :250].contiguous().to(DEV)).cpu()
-    assert torch.equal(pre, a[:, :, :250])
+    # a prefix of whole chunks (256 = 4 x 64) gives the same rows bit for bit in both forms
+    pre = ea.attn_linear_fwd(q[:, :, :256].contiguous().to(DEV), k[:, :, :256].contiguous().to(DEV),
+                             v[:, :, :256].contiguous().to(DEV), chunked=chunked).cpu()
+    assert torch.equal(pre, a[:, :, :256])
 
 
-def test_full_size_workload():
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
+def test_full_size_workload(chunked):
     """The benchmark shape (2 x 32 x 8192, E = M = 64, feature map): two heads in full
     against the oracle, in the benchmark's launch."""
     B, H, N, E, M = 2, 32, 8192, 64, 64
     q, k, v = inputs(B, H, N, E, M, seed=11)
-    say(f"[linear] full size {(B, H, N, E, M)}")
-    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    say(f"[linear] full size {(B, H, N, E, M)} chunked={chunked}")
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunked=chunked).cpu()
     assert torch.isfinite(o).all()
     for (b, h) in [(0, 0), (1, 31)]:
         sl = (slice(b, b + 1), slice(h, h + 1))
         o_ref = oracle.linear_attn(q[sl], k[sl], v[sl], True, 1e-6)
         err = np.abs(o[sl].double().numpy() - o_ref)
-        bar = bound(q[sl], k[sl], v[sl], True, 1e-6, o_ref)
+        bar = bound(q[sl], k[sl], v[sl], True, 1e-6, o_ref, chunked)
         say(f"[linear]   head ({b},{h}): max err {err.max():.3e}, max err / bound {(err / bar).max():.4f}")
         assert (err / bar).max() <= 1.0
