@@ -19,8 +19,9 @@ key lengths, a boolean mask packed once before timing), counted at 4*d flops per
 visible (query, key) pair.
 
 With --workload l1 a step is one call of attn_linear_fwd (causal linear
-attention, fp32), a scan bound by HBM: the value is algorithmic GB/s (read q, k,
-v and write o once) against the 8 TB/s peak.
+attention, fp32; the chunked form: chunk states, prefix over chunks, outputs, on
+a workspace allocated before timing), bound by HBM: the value is algorithmic GB/s
+(read q, k, v and write o once) against the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -373,9 +374,11 @@ def bench_linear(args, lw):
     dev = "cuda:0"
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(vd)
+    # the chunked form's workspace, allocated once outside the timed region
+    ws = torch.empty(ea.linear_workspace_bytes(lw.B, lw.H, lw.N, lw.E, lw.M), dtype=torch.uint8, device=dev)
 
     def step():
-        ea.attn_linear_fwd(qd, kd, vd, feature_map=lw.feature_map, eps=lw.eps, out=o)
+        ea.attn_linear_fwd(qd, kd, vd, feature_map=lw.feature_map, eps=lw.eps, out=o, workspace=ws)
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     wall, kernel_ms = time_steps(step, args.steps, args.warmup)
@@ -395,6 +398,7 @@ def bench_linear(args, lw):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "algorithmic_bytes": lw.io_bytes, "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
                      "fp32_tflops": round(lw.flops / avg_kernel_s / 1e12, 2),
+                     "workspace_bytes": ws.numel(),
                      "kernel_source_sha": kernel_source_hash()},
     }
     if args.cpu_seconds > 0 and args.cpu_heads != 0:
