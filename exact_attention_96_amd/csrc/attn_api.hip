@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <utility>
 
 #include "fwd_f32.hpp"
 #include "bwd_mfma.hpp"
@@ -355,11 +356,15 @@ hipError_t launch_linear_chunked(const attn::LinChunkArgs &a, int bh, hipStream_
     typedef attn::LinChunk<E> K;
     const int grid = bh * a.n_chunks;  // bounded by the checks in attn_linear_fwd
     const int s_lds = K::states_lds(a.M), o_lds = K::outputs_lds(a.M);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn::attn_linear_states_kernel<E>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, s_lds);
+    // the LDS these kernels take depends on M: each is opted in once per device to the
+    // whole 160 KB (the caller has checked that both sizes fit)
+    struct StatesTag {};
+    struct OutputsTag {};
+    hipError_t e = opt_in_lds<std::pair<K, StatesTag>>(
+        reinterpret_cast<const void *>(&attn::attn_linear_states_kernel<E>), 160 * 1024);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn::attn_linear_outputs_kernel<E>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, o_lds);
+    e = opt_in_lds<std::pair<K, OutputsTag>>(reinterpret_cast<const void *>(&attn::attn_linear_outputs_kernel<E>),
+                                             160 * 1024);
     if (e != hipSuccess) return e;
     e = launch(&attn::attn_linear_states_kernel<E>, grid, K::THREADS, s_lds, stream, a);
     if (e != hipSuccess) return e;
@@ -369,13 +374,19 @@ hipError_t launch_linear_chunked(const attn::LinChunkArgs &a, int bh, hipStream_
     return launch(&attn::attn_linear_outputs_kernel<E>, grid, K::THREADS, o_lds, stream, a);
 }
 
-// LDS of the chunked output kernel for (E, M); the chunked form is used only where it fits.
+// LDS of the larger of the chunked state and output kernels for (E, M); the chunked
+// form is used only where both fit.
+template <int E>
+int linear_chunk_lds_e(int M) {
+    const int s = attn::LinChunk<E>::states_lds(M), o = attn::LinChunk<E>::outputs_lds(M);
+    return s > o ? s : o;
+}
 int linear_chunk_lds(int E, int M) {
     switch (E) {
-        case 16: return attn::LinChunk<16>::outputs_lds(M);
-        case 32: return attn::LinChunk<32>::outputs_lds(M);
-        case 64: return attn::LinChunk<64>::outputs_lds(M);
-        default: return attn::LinChunk<128>::outputs_lds(M);
+        case 16: return linear_chunk_lds_e<16>(M);
+        case 32: return linear_chunk_lds_e<32>(M);
+        case 64: return linear_chunk_lds_e<64>(M);
+        default: return linear_chunk_lds_e<128>(M);
     }
 }
 
