@@ -289,6 +289,9 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
     if mask is not None:
         if not isinstance(mask, torch.Tensor) or mask.device != q.device:
             raise ValueError("mask must be a tensor on q's device")
+        if mask.dim() != 4 or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H) \
+                or tuple(mask.shape[2:]) != (Nq, Nk):
+            raise ValueError(f"mask of shape {tuple(mask.shape)} does not match [{B} or 1, {H} or 1, {Nq}, {Nk}]")
         mask_bits = pack_mask(mask)
     sb = sh = 0
     mptr = tptr = None

@@ -149,3 +149,34 @@ def test_full_size_workload(chunked):
         bar = bound(q[sl], k[sl], v[sl], True, 1e-6, o_ref, chunked)
         say(f"[linear]   head ({b},{h}): max err {err.max():.3e}, max err / bound {(err / bar).max():.4f}")
         assert (err / bar).max() <= 1.0
+
+
+def test_side_stream_and_caller_workspace():
+    """Both forms on a side stream; the chunked one on a workspace the caller passes."""
+    q, k, v = inputs(1, 2, 300, 32, 32, seed=13)
+    o_ref = oracle.linear_attn(q, k, v, True, 1e-6)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+        ws = torch.empty(ea.linear_workspace_bytes(1, 2, 300, 32, 32), dtype=torch.uint8, device=DEV)
+        s.synchronize()
+        a = ea.attn_linear_fwd(qd, kd, vd, workspace=ws)
+        b = ea.attn_linear_fwd(qd, kd, vd, chunked=False)
+    s.synchronize()
+    for o, chunked in ((a, True), (b, False)):
+        err = np.abs(o.cpu().double().numpy() - o_ref)
+        assert (err / bound(q, k, v, True, 1e-6, o_ref, chunked)).max() <= 1.0
+
+
+def test_binding_rejects_bad_arguments():
+    q = torch.zeros(1, 1, 8, 64, device=DEV)
+    with pytest.raises(ValueError):       # not float32
+        ea.attn_linear_fwd(q.half(), q.half(), q.half())
+    with pytest.raises(ValueError):       # k shaped differently from q
+        ea.attn_linear_fwd(q, q[..., :32].contiguous(), q)
+    with pytest.raises(ValueError):       # workspace too small
+        ea.attn_linear_fwd(q, q, q, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    with pytest.raises(ea.AttnError) as e:
+        z = torch.zeros(1, 1, 8, 48, device=DEV)
+        ea.attn_linear_fwd(z, z, z)
+    assert e.value.status == ea.ATTN_EUNSUPPORTED

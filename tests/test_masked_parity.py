@@ -216,3 +216,38 @@ def test_masked_scales(scale, dtype, d):
     q, k, v = random_qkv_lens(2, 2, 200, 333, d, dtype, seed=91)
     mask = random_mask("bernoulli", 1, 2, 200, 333, seed=92, p=0.3)
     parity(q, k, v, mask, True, scale, dtype, f"masked scale {scale}")
+
+
+def test_side_stream():
+    """attn_mask_pack and attn_fwd_masked on a side stream (torch's current stream there)."""
+    q, k, v = random_qkv_lens(1, 3, 257, 500, 128, "f16", seed=101)
+    mask = random_mask("bernoulli", 1, 1, 257, 500, seed=102, p=0.5)
+    s = torch.cuda.Stream()
+    say("[masked] f16 on a side stream")
+    with torch.cuda.stream(s):
+        qd, kd, vd, md = (t.to(DEV, non_blocking=False) for t in (q, k, v, mask))
+        s.synchronize()
+        o, lse = ea.attn_fwd_masked(qd, kd, vd, mask=md, causal=True, scale=0.0884)
+    s.synchronize()
+    o_ref, lse_ref = oracle.attn_masked(q, k, v, 0.0884, True, mask)
+    compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "f16", "side stream")
+
+
+def test_binding_rejects_bad_arguments():
+    q = torch.zeros(1, 2, 8, 64, device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 12, 64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):       # k and v of different lengths
+        ea.attn_fwd_masked(q, k, k[:, :, :10])
+    with pytest.raises(TypeError):        # mixed dtypes
+        ea.attn_fwd_masked(q, k, k.half())
+    with pytest.raises(ValueError):       # mask of the wrong shape
+        ea.attn_fwd_masked(q, k, k, mask=torch.ones(1, 2, 8, 11, dtype=torch.bool, device=DEV))
+    with pytest.raises(ValueError):       # mask and packed bits together
+        m = torch.ones(1, 1, 8, 12, dtype=torch.bool, device=DEV)
+        ea.attn_fwd_masked(q, k, k, mask=m, mask_bits=ea.pack_mask(m))
+    with pytest.raises(TypeError):        # a float mask is not a boolean mask
+        ea.pack_mask(torch.ones(1, 1, 8, 12, device=DEV))
+    with pytest.raises(ea.AttnError) as e:
+        z = torch.zeros(1, 1, 8, 96, device=DEV, dtype=torch.bfloat16)
+        ea.attn_fwd_masked(z, z, z)
+    assert e.value.status == ea.ATTN_EUNSUPPORTED
