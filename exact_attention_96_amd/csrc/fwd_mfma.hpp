@@ -148,8 +148,9 @@ __device__ __forceinline__ float lane_swap32_add(float x) {
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
-// V^T reads issued before the first score MFMA of a matrix phase
-constexpr int kGemmFirstReads = 8;
+// V^T reads issued before the first score MFMA of a matrix phase (interleaved timings on
+// three boards: 0 beats 2 by ~0.4 %, 8 by ~1.5 %; 12 and 16 lose 16 % and 40 %)
+constexpr int kGemmFirstReads = 0;
 
 // Scheduling groups: N single MFMAs, each followed by up to PER of the LEFT
 // remaining LDS reads.
@@ -297,13 +298,13 @@ struct MfmaFwd {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc) s[h] = M::mma(kf[h][cc], S.qf[cc], s[h]);
-        // Issue order: a first batch of V^T reads, then each score MFMA followed by
-        // two more reads (a fragment is two transposing reads).
+        // Issue order: kGemmFirstReads V^T reads (none), then each score MFMA followed by
+        // its share of the reads (two: a fragment is two transposing reads).
         constexpr int NV = 8 * DB;       // transposing reads per unit
         constexpr int NS = 2 * DC;       // score MFMAs per unit
         constexpr int FIRST = kGemmFirstReads < NV ? kGemmFirstReads : NV;
         constexpr int PER = (NV - FIRST + NS - 1) / NS;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST, 0);
+        if constexpr (FIRST > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST, 0);
         sched_mfma_reads<NS, PER, NV - FIRST>();
         constexpr int NP = 4 * DB;       // P V MFMAs per unit
         constexpr int CHUNK = NP / KVLOADS;
