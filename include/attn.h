@@ -1,6 +1,8 @@
 /*
  * attn.h — C ABI of the exact attention library for MI355X (gfx950):
- * forward (attn_fwd) and backward (attn_bwd).
+ * forward (attn_fwd), backward (attn_bwd), forward with unequal query/key
+ * lengths and boolean masks (attn_fwd_masked, attn_mask_pack), and causal
+ * linear attention (attn_linear_fwd, attn_linear_workspace_bytes).
  *
  * The operation is exact scaled-dot-product attention, one (batch, head) at a
  * time:
