@@ -374,21 +374,27 @@ hipError_t launch_linear_chunked(const attn::LinChunkArgs &a, int bh, hipStream_
     return launch(&attn::attn_linear_outputs_kernel<E>, grid, K::THREADS, o_lds, stream, a);
 }
 
-// LDS of the larger of the chunked state and output kernels for (E, M); the chunked
-// form is used only where both fit.
+// The matrix-core chunk kernels (E >= 32) use no LDS.
+template <int E>
+hipError_t launch_linear_chunked_mfma(const attn::LinChunkArgs &a, int bh, hipStream_t stream) {
+    const int grid = bh * a.n_chunks;  // bounded by the checks in attn_linear_fwd
+    const int tiles = attn::LinChunkMfma<E>::STATE_TILES_PER_E * ((a.M + 31) / 32);
+    hipError_t e = launch(&attn::attn_linear_states_mfma_kernel<E>, grid * tiles, 64, 0, stream, a);
+    if (e != hipSuccess) return e;
+    const int per_chunk = E * a.M + E, bph = (per_chunk + 255) / 256;
+    e = launch(&attn::attn_linear_prefix_kernel, bh * bph, 256, 0, stream, a.ws, a.n_chunks, per_chunk, bph);
+    if (e != hipSuccess) return e;
+    return launch(&attn::attn_linear_outputs_mfma_kernel<E>, grid, 256, 0, stream, a);
+}
+
+// LDS of the larger of the chunked state and output kernels for (E, M); the LDS form
+// (E = 16) is used only where both fit.
 template <int E>
 int linear_chunk_lds_e(int M) {
     const int s = attn::LinChunk<E>::states_lds(M), o = attn::LinChunk<E>::outputs_lds(M);
     return s > o ? s : o;
 }
-int linear_chunk_lds(int E, int M) {
-    switch (E) {
-        case 16: return linear_chunk_lds_e<16>(M);
-        case 32: return linear_chunk_lds_e<32>(M);
-        case 64: return linear_chunk_lds_e<64>(M);
-        default: return linear_chunk_lds_e<128>(M);
-    }
-}
+int linear_chunk_lds(int E, int M) { return E == 16 ? linear_chunk_lds_e<16>(M) : 0; }
 
 extern "C" ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M) {
     if (B < 1 || H < 1 || N < 1 || E < 1 || M < 1) return -1;
@@ -421,7 +427,13 @@ extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const fl
     if (grid > (uint64_t)INT32_MAX || (uint64_t)N * (uint64_t)(E > M ? E : M) > (uint64_t)INT32_MAX)
         return ATTN_EUNSUPPORTED;
     const uint64_t chunks = ((uint64_t)N + 63) / 64;
-    if (workspace && linear_chunk_lds(E, M) <= 160 * 1024 && (uint64_t)B * (uint64_t)H * chunks <= (uint64_t)INT32_MAX &&
+    // the matrix-core chunk kernels address a head's v and o, and a chunk's state, with
+    // 32-bit byte offsets below 2^31 (rows up to one chunk past the end included)
+    const uint64_t wide = (uint64_t)(E > M ? E : M);
+    const bool mfma_ok = E >= 32 && ((uint64_t)N + 128) * wide * 4 < (1ull << 31) &&
+                         ((uint64_t)E * M + E) * 4 < (1ull << 31) &&
+                         (uint64_t)B * H * chunks * (E / 32) * ((M + 31) / 32) <= (uint64_t)INT32_MAX;
+    if (workspace && (mfma_ok || (E == 16 && linear_chunk_lds(E, M) <= 160 * 1024)) && (uint64_t)B * (uint64_t)H * chunks <= (uint64_t)INT32_MAX &&
         (uint64_t)B * (uint64_t)H * (((uint64_t)E * M + E + 255) / 256) <= (uint64_t)INT32_MAX) {
         attn::LinChunkArgs c;
         c.q = q;
@@ -438,9 +450,9 @@ extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const fl
         hipError_t e;
         switch (E) {
             case 16: e = launch_linear_chunked<16>(c, bh, stream); break;
-            case 32: e = launch_linear_chunked<32>(c, bh, stream); break;
-            case 64: e = launch_linear_chunked<64>(c, bh, stream); break;
-            default: e = launch_linear_chunked<128>(c, bh, stream); break;
+            case 32: e = launch_linear_chunked_mfma<32>(c, bh, stream); break;
+            case 64: e = launch_linear_chunked_mfma<64>(c, bh, stream); break;
+            default: e = launch_linear_chunked_mfma<128>(c, bh, stream); break;
         }
         return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
     }

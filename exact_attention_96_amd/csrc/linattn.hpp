@@ -437,6 +437,207 @@ __global__ __launch_bounds__(256, 2) void attn_linear_outputs_kernel(LinChunkArg
     LinChunk<E>::outputs(a);
 }
 
+// The same chunk kernels on the fp32 matrix cores (E in {32, 64, 128}), with no LDS.
+// v_mfma_f32_32x32x2_f32 adds a 32 x 32 product over 2 terms: lane l gives row l % 32 of
+// the left operand and column l % 32 of the right one, each at term l / 32, and keeps 16
+// entries of the result: column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
+// A sum over e (or over tokens) may visit its terms in any order, so each lane takes
+// the half h = l / 32 of the terms in one contiguous run: its operands are 16-byte loads
+// of one row, straight from global memory into registers.
+//   states:  per (head, chunk), dS = phi(K)^T V in 32 x 32 tiles (e, m) over the
+//            chunk's 64 tokens (half h: tokens 32 h ... 32 h + 31), and z = sum of phi(k).
+//   outputs: wave w of a chunk owns query rows 32 (w & 1) ... + 31 and the value-column
+//            blocks w >> 1, (w >> 1) + 2, ...  It first forms A^T = phi(K) phi(Q)^T for
+//            the key blocks up to its own (the causal zero block is skipped; the diagonal
+//            block is masked).  In that layout a lane holds one query row and 16 keys,
+//            which are exactly the left operand of A V for those 16 keys, so A stays in
+//            registers; the normaliser's row sums are in-lane plus one exchange.
+template <int E>
+struct LinChunkMfma {
+    static constexpr int TC = 64, THREADS = 256, HE = E / 2;
+    static_assert(E % 32 == 0 && HE % 4 == 0, "E in {32, 64, 128}");
+    static __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(x); }
+    static __device__ __forceinline__ f32x16_t mma(float a, float b, const f32x16_t &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // x[s] = (phi of) row[s], s < HE; zeros for a row past the sequence end
+    static __device__ __forceinline__ void load_half(float (&x)[HE], const float *row, bool ok, bool fm) {
+#pragma unroll
+        for (int j = 0; j < HE / 4; ++j) {
+            const f32x4_t v = ok ? *reinterpret_cast<const f32x4_t *>(row + 4 * j) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * j + i] = v[i];
+        }
+        if (fm && ok)
+#pragma unroll
+            for (int s = 0; s < HE; ++s) x[s] = phi(x[s]);
+    }
+
+    // One wave per (head, chunk, tile (e block, m block)) of dS over the chunk's tokens.
+    // The wave loads rows [c0, c0 + 64) x 32 columns of phi(K) and of V with 16-byte
+    // loads (eight rows per load; zeros past the sequence end or the row), then stages
+    // them in LDS 32 tokens at a time (8 KB per wave, so LDS does not limit occupancy)
+    // and reads the operand columns from there.  Token of term (h, s) within a half is
+    // 2 s + h, so the two half-waves read adjacent LDS rows (distinct banks).
+    static constexpr int STATE_TILES_PER_E = E / 32;
+    static __device__ __forceinline__ void load_rows(f32x4_t (&val)[8], const float *src, int c0, int N, int W,
+                                                     int x0, bool fm, int lane) {
+        const int q = lane & 7, r0 = lane >> 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = c0 + r0 + 8 * j;
+            const bool ok = t < N && x0 + 4 * q < W;
+            val[j] = ok ? *reinterpret_cast<const f32x4_t *>(src + (size_t)t * W + x0 + 4 * q)
+                        : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            if (fm && ok)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[j][i] = phi(val[j][i]);
+        }
+    }
+    static __device__ void states(const LinChunkArgs &a) {
+        __shared__ __attribute__((aligned(16))) float lds[2 * 32 * 32];
+        const int N = a.N, M = a.M;
+        const bool fm = a.feature_map != 0;
+        const int lane = threadIdx.x, col = lane & 31, h = lane >> 5, q = lane & 7, r0 = lane >> 3;
+        const int nm = (M + 31) / 32, tiles = STATE_TILES_PER_E * nm;
+        const int chunk = blockIdx.x / tiles, tile = blockIdx.x - chunk * tiles;
+        const int bh = chunk / a.n_chunks, c = chunk - bh * a.n_chunks, c0 = c * TC;
+        const int eb = tile / nm, mb = tile - eb * nm, e = 32 * eb + col, m = 32 * mb + col;
+        float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
+        float *Ks = lds, *Vs = lds + 32 * 32;
+        f32x4_t kv4[8], vv4[8];
+        load_rows(kv4, a.k + (size_t)bh * N * E, c0, N, E, 32 * eb, fm, lane);
+        load_rows(vv4, a.v + (size_t)bh * N * M, c0, N, M, 32 * mb, false, lane);
+        f32x16_t acc = {};
+        float zs = 0.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            // rows 32 half ... + 31 of the chunk are loads j = 4 half ... 4 half + 3
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *reinterpret_cast<f32x4_t *>(Ks + (r0 + 8 * j) * 32 + 4 * q) = kv4[4 * half + j];
+                *reinterpret_cast<f32x4_t *>(Vs + (r0 + 8 * j) * 32 + 4 * q) = vv4[4 * half + j];
+            }
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float kv = Ks[(2 * s + h) * 32 + col];
+                acc = mma(kv, Vs[(2 * s + h) * 32 + col], acc);
+                zs += kv;
+            }
+        }
+        if (m < M)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) W[(size_t)(32 * eb + 8 * (r >> 2) + 4 * h + (r & 3)) * M + m] = acc[r];
+        if (mb == 0) {
+            zs += __shfl_xor(zs, 32);
+            if (h == 0) W[(size_t)E * M + e] = zs;
+        }
+    }
+
+    // Raw buffer accesses (stride 0): the resource holds the base and the byte count, a
+    // lane gives a 32-bit byte offset, and an offset at or past the count reads 0 and
+    // drops a store.  Rows past the sequence end and value columns past M need no branch.
+    typedef __amdgpu_buffer_rsrc_t rsrc_t;
+    static constexpr uint32_t kOff = 0x80000000u;  // an offset past every resource used here
+    static __device__ __forceinline__ rsrc_t rsrc(const float *p, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
+    }
+    static __device__ __forceinline__ float bload(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
+    }
+
+    static __device__ void outputs(const LinChunkArgs &a) {
+        const int N = a.N, M = a.M;
+        const bool fm = a.feature_map != 0;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 31, h = lane >> 5;
+        const int bh = blockIdx.x / a.n_chunks, c = blockIdx.x - bh * a.n_chunks, c0 = c * TC;
+        const int tb = w & 1, t0 = c0 + 32 * tb;
+        const float *qh = a.q + (size_t)bh * N * E, *kh = a.k + (size_t)bh * N * E;
+        const float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
+        // the head's v and o, and the chunk's state (the host keeps each under 2^31 bytes)
+        const rsrc_t vr = rsrc(a.v + (size_t)bh * N * M, (uint32_t)N * M * 4);
+        const rsrc_t orr = rsrc(a.o + (size_t)bh * N * M, (uint32_t)N * M * 4);
+        const rsrc_t sr = rsrc(W, (uint32_t)E * M * 4);
+        float qf[HE];
+        load_half(qf, qh + (size_t)(t0 + col) * E + h * HE, t0 + col < N, fm);
+        // A^T of key block 0 (and 1 for the second row block); lane: query t0 + col,
+        // keys 8 (r / 4) + 4 h + r % 4 of the block
+        f32x16_t a0 = {}, a1 = {};
+        {
+            float kf[HE];
+            load_half(kf, kh + (size_t)(c0 + col) * E + h * HE, c0 + col < N, fm);
+#pragma unroll
+            for (int s = 0; s < HE; ++s) a0 = mma(kf[s], qf[s], a0);
+        }
+        if (tb) {
+            float kf[HE];
+            load_half(kf, kh + (size_t)(c0 + 32 + col) * E + h * HE, c0 + 32 + col < N, fm);
+#pragma unroll
+            for (int s = 0; s < HE; ++s) a1 = mma(kf[s], qf[s], a1);
+        }
+        // causal: key p of the diagonal block is visible to query col when p <= col
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const bool hide = 8 * (r >> 2) + 4 * h + (r & 3) > col;
+            if (tb) a1[r] = hide ? 0.f : a1[r];
+            else a0[r] = hide ? 0.f : a0[r];
+        }
+        // normaliser of query t0 + col: phi(q) . z + sum of its row of A, plus eps
+        float inv = 1.f;
+        if (fm) {
+            float d = 0.f;
+            const float *z = W + (size_t)E * M + h * HE;
+#pragma unroll
+            for (int j = 0; j < HE / 4; ++j) {
+                const f32x4_t zz = *reinterpret_cast<const f32x4_t *>(z + 4 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d = fmaf(qf[4 * j + i], zz[i], d);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) d += a0[r] + a1[r];
+            d += __shfl_xor(d, 32);
+            inv = 1.f / (d + a.eps);
+        }
+        const uint32_t M4 = (uint32_t)M * 4;
+        for (int mb = w >> 1; 32 * mb < M; mb += 2) {
+            const int m = 32 * mb + col;
+            const bool okm = m < M;
+            f32x16_t acc = {};
+            // phi(Q) S_c: term e = h E/2 + s
+            const uint32_t so = okm ? (uint32_t)(h * HE) * M4 + 4u * m : kOff;
+#pragma unroll
+            for (int s = 0; s < HE; ++s) acc = mma(qf[s], bload(sr, so + s * M4), acc);
+            // A V over the chunk's keys up to this row block: term s is key 8 (s / 4) + 4 h + s % 4
+            const uint32_t vo = okm ? (uint32_t)(c0 + 4 * h) * M4 + 4u * m : kOff;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) acc = mma(a0[s], bload(vr, vo + (8 * (s >> 2) + (s & 3)) * M4), acc);
+            if (tb)
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    acc = mma(a1[s], bload(vr, vo + (32 + 8 * (s >> 2) + (s & 3)) * M4), acc);
+            const uint32_t oo = okm ? (uint32_t)(t0 + 4 * h) * M4 + 4u * m : kOff;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + (r & 3);  // row t0 + 4 h + i
+                bstore(orr, oo + i * M4, acc[r] * __shfl(inv, i + 4 * h));
+            }
+        }
+    }
+};
+
+template <int E>
+__global__ __launch_bounds__(64) void attn_linear_states_mfma_kernel(LinChunkArgs a) {
+    LinChunkMfma<E>::states(a);
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void attn_linear_outputs_mfma_kernel(LinChunkArgs a) {
+    LinChunkMfma<E>::outputs(a);
+}
+
 // (2) exclusive prefix over the chunks of each head, in place: thread x of the head
 // owns workspace entry x of every chunk (state and key sum alike).
 __global__ __launch_bounds__(256) void attn_linear_prefix_kernel(float *ws, int n_chunks, int per_chunk,

@@ -253,9 +253,11 @@ ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o
  *            into chunks of 64 tokens: per chunk phi(K)^T V and the key sum go to
  *            the workspace, an exclusive prefix over the chunks follows, and each
  *            chunk's outputs are phi(Q) times its prefix plus the causal
- *            in-chunk product (three launches, parallel over chunks).  Without
- *            it (or where the chunk tiles do not fit in LDS: E * M large) one
- *            sequential scan per (head, 16 value columns) runs instead.
+ *            in-chunk product (three launches, parallel over chunks; for E >= 32
+ *            on the fp32 matrix cores).  Without it one sequential scan per
+ *            (head, 16 value columns) runs instead; so it does where the chunk
+ *            form's limits are exceeded: for E >= 32, (N + 128) * max(E, M) * 4
+ *            and (E * M + E) * 4 below 2^31 bytes; for E = 16, tiles within LDS.
  *   workspace_bytes  size of workspace in bytes (ignored when it is NULL).
  *   stream   HIP stream the work is enqueued on.
  *

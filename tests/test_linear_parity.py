@@ -77,7 +77,8 @@ def check(q, k, v, fm, eps, what, chunked=True):
 
 
 SHAPES = [(1, 1, 1, 16, 16), (1, 2, 31, 32, 16), (2, 2, 100, 64, 64), (1, 3, 257, 128, 32),
-          (2, 1, 1000, 64, 48), (1, 1, 33, 16, 128), (1, 2, 700, 128, 64)]
+          (2, 1, 1000, 64, 48), (1, 1, 33, 16, 128), (1, 2, 700, 128, 64), (1, 1, 129, 32, 80),
+          (1, 2, 64, 128, 128)]
 
 
 @pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "scan"])
@@ -105,11 +106,21 @@ def test_wide_inputs(chunked):
     check(q, k, v, True, 1e-6, "wide inputs", chunked)
 
 
-def test_large_value_width_falls_back_to_the_scan():
-    """E = 128 with M = 256 does not fit the chunk tiles in LDS: the call with a
-    workspace runs the scan and meets the scan's bound."""
+def test_large_value_width():
+    """E = 128 with M = 256: eight value-column blocks, four per wave, in the chunked
+    matrix-core form."""
     q, k, v = inputs(1, 1, 200, 128, 256, seed=12)
     check(q, k, v, True, 1e-6, "E 128 M 256", True)
+
+
+def test_lds_chunk_limit_falls_back_to_the_scan():
+    """E = 16 with M = 512 does not fit the LDS chunk tiles of that width: the call with
+    a workspace runs the scan and meets the scan's (tighter) bound."""
+    q, k, v = inputs(1, 1, 200, 16, 512, seed=13)
+    check(q, k, v, True, 1e-6, "E 16 M 512", False)
+    o = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunked=True).cpu()
+    o_scan = ea.attn_linear_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunked=False).cpu()
+    assert torch.equal(o, o_scan)
 
 
 def test_constant_values_and_zero_queries():
