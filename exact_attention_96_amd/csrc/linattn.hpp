@@ -563,28 +563,40 @@ struct LinChunkMfma {
         const rsrc_t sr = rsrc(W, (uint32_t)E * M * 4);
         float qf[HE];
         load_half(qf, qh + (size_t)(t0 + col) * E + h * HE, t0 + col < N, fm);
-        // A^T of key block 0 (and 1 for the second row block); lane: query t0 + col,
-        // keys 8 (r / 4) + 4 h + r % 4 of the block
+        // The chunk's three nonzero blocks of A^T (key block, query block) = (0, 0), (0, 1),
+        // (1, 1) are formed once, by waves 0, 1 and 3, and exchanged through LDS; lane:
+        // query col of the block, keys 8 (r / 4) + 4 h + r % 4.
+        __shared__ f32x4_t ash[3][4][64];
+        const int role = w == 0 ? 0 : w == 1 ? 1 : w == 3 ? 2 : -1;
+        if (role >= 0) {
+            const int kb = role == 2 ? 32 : 0;
+            float kf[HE];
+            load_half(kf, kh + (size_t)(c0 + kb + col) * E + h * HE, c0 + kb + col < N, fm);
+            f32x16_t ab = {};
+#pragma unroll
+            for (int s = 0; s < HE; ++s) ab = mma(kf[s], qf[s], ab);
+            if (role != 1)  // diagonal block: key p is visible to query col when p <= col
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ab[r] = 8 * (r >> 2) + 4 * h + (r & 3) > col ? 0.f : ab[r];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                ash[role][g][lane] = (f32x4_t){ab[4 * g], ab[4 * g + 1], ab[4 * g + 2], ab[4 * g + 3]};
+        }
+        __syncthreads();
         f32x16_t a0 = {}, a1 = {};
-        {
-            float kf[HE];
-            load_half(kf, kh + (size_t)(c0 + col) * E + h * HE, c0 + col < N, fm);
 #pragma unroll
-            for (int s = 0; s < HE; ++s) a0 = mma(kf[s], qf[s], a0);
-        }
-        if (tb) {
-            float kf[HE];
-            load_half(kf, kh + (size_t)(c0 + 32 + col) * E + h * HE, c0 + 32 + col < N, fm);
+        for (int g = 0; g < 4; ++g) {
+            const f32x4_t x = ash[tb][g][lane];
 #pragma unroll
-            for (int s = 0; s < HE; ++s) a1 = mma(kf[s], qf[s], a1);
+            for (int i = 0; i < 4; ++i) a0[4 * g + i] = x[i];
         }
-        // causal: key p of the diagonal block is visible to query col when p <= col
+        if (tb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const bool hide = 8 * (r >> 2) + 4 * h + (r & 3) > col;
-            if (tb) a1[r] = hide ? 0.f : a1[r];
-            else a0[r] = hide ? 0.f : a0[r];
-        }
+            for (int g = 0; g < 4; ++g) {
+                const f32x4_t x = ash[2][g][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a1[4 * g + i] = x[i];
+            }
         // normaliser of query t0 + col: phi(q) . z + sum of its row of A, plus eps
         float inv = 1.f;
         if (fm) {
