@@ -500,7 +500,10 @@ struct LinChunkMfma {
         const bool fm = a.feature_map != 0;
         const int lane = threadIdx.x, col = lane & 31, h = lane >> 5, q = lane & 7, r0 = lane >> 3;
         const int nm = (M + 31) / 32, tiles = STATE_TILES_PER_E * nm;
-        const int chunk = blockIdx.x / tiles, tile = blockIdx.x - chunk * tiles;
+        // each XCD takes a contiguous range of tiles, so the tiles of a chunk (which read
+        // the same rows of phi(K) and V) share one L2
+        const int lin = xcd_contiguous(blockIdx.x, gridDim.x);
+        const int chunk = lin / tiles, tile = lin - chunk * tiles;
         const int bh = chunk / a.n_chunks, c = chunk - bh * a.n_chunks, c0 = c * TC;
         const int eb = tile / nm, mb = tile - eb * nm, e = 32 * eb + col, m = 32 * mb + col;
         float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
