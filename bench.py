@@ -41,6 +41,7 @@ PEAK_MFMA_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 409
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_hbm_traffic.txt")
+TRAFFIC_FILE_LINEAR = os.path.join(ROOT, "profiles", "attn_linear_fwd_l1_hbm_traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -51,13 +52,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken on
-    the current kernel source and this workload; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload_name: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch (per call of the entry point) from the committed counter
+    summary, if it was taken on the current kernel source and this workload; else None."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for ln in f:
             if "=" in ln and not ln.lstrip().startswith("#"):
                 k, v = ln.split("=", 1)
@@ -80,21 +81,41 @@ def _counter_avg(path: str, counter: str, name_part: str) -> float:
     return sum(vals) / len(vals)
 
 
+def _counter_step(path: str, counter: str, name_part: str) -> float:
+    """Sum over the kernels whose name contains name_part of each one's mean per-dispatch
+    counter value: the counter per call of an entry point that launches each once."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"no {counter} rows for '{name_part}' in {path}")
+    return sum(sum(v) / len(v) for v in per.values())
+
+
 def summarize_traffic(args) -> None:
     """Write the HBM traffic summary from two attention runs (FETCH_SIZE, WRITE_SIZE) and the
     same two counters on a plain device copy of known size (calibration)."""
-    from exact_attention_96_amd.workloads import WORKLOADS
-    w = WORKLOADS[args.workload]
-    kern = "attn_fwd_mfma_kernel" if w.dtype != "f32" else "attn_fwd_f32_kernel"
-    fetch_kib = _counter_avg(args.fetch_csv, "FETCH_SIZE", kern)
-    write_kib = _counter_avg(args.write_csv, "WRITE_SIZE", kern)
+    from exact_attention_96_amd.workloads import LINEAR_WORKLOADS, WORKLOADS
+    if args.workload in LINEAR_WORKLOADS:
+        # the chunked form's launches of one call, summed
+        w = LINEAR_WORKLOADS[args.workload]
+        kern = "attn_linear_"
+        fetch_kib = _counter_step(args.fetch_csv, "FETCH_SIZE", kern)
+        write_kib = _counter_step(args.write_csv, "WRITE_SIZE", kern)
+    else:
+        w = WORKLOADS[args.workload]
+        kern = "attn_fwd_mfma_kernel" if w.dtype != "f32" else "attn_fwd_f32_kernel"
+        fetch_kib = _counter_avg(args.fetch_csv, "FETCH_SIZE", kern)
+        write_kib = _counter_avg(args.write_csv, "WRITE_SIZE", kern)
     copy_fetch_kib = _counter_avg(args.copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
     copy_write_kib = _counter_avg(args.copy_write_csv, "WRITE_SIZE", "copyBuffer")
     fetch_factor = args.copy_bytes / (copy_fetch_kib * 1024)
     write_factor = args.copy_bytes / (copy_write_kib * 1024)
     hbm = fetch_kib * 1024 * fetch_factor + write_kib * 1024 * write_factor
     lines = [
-        f"# HBM traffic of {kern} on {w.name}",
+        f"# HBM traffic of {kern}{'* (every launch of one call)' if kern == 'attn_linear_' else ''} on {w.name}",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (rocprofv3 --pmc, one counter per run),",
         "# scaled by the ratio of known bytes to counter bytes on a device copy of copy_bytes.",
         f"workload = {w.name}",
@@ -399,7 +420,8 @@ def bench_linear(args, lw):
         "config": {"workload": lw.name, "B": lw.B, "H": lw.H, "N": lw.N, "E": lw.E, "M": lw.M,
                    "feature_map": lw.feature_map, "eps": lw.eps},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(lw.name, TRAFFIC_FILE_LINEAR),
                      "algorithmic_bytes": lw.io_bytes, "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
                      "fp32_tflops": round(lw.flops / avg_kernel_s / 1e12, 2),
                      "workspace_bytes": ws.numel(),
