@@ -437,21 +437,23 @@ __global__ __launch_bounds__(256, 2) void attn_linear_outputs_kernel(LinChunkArg
     LinChunk<E>::outputs(a);
 }
 
-// The same chunk kernels on the fp32 matrix cores (E in {32, 64, 128}), with no LDS.
+// The same chunk kernels on the fp32 matrix cores (E in {32, 64, 128}).
 // v_mfma_f32_32x32x2_f32 adds a 32 x 32 product over 2 terms: lane l gives row l % 32 of
 // the left operand and column l % 32 of the right one, each at term l / 32, and keeps 16
 // entries of the result: column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
 // A sum over e (or over tokens) may visit its terms in any order, so each lane takes
 // the half h = l / 32 of the terms in one contiguous run: its operands are 16-byte loads
 // of one row, straight from global memory into registers.
-//   states:  per (head, chunk), dS = phi(K)^T V in 32 x 32 tiles (e, m) over the
-//            chunk's 64 tokens (half h: tokens 32 h ... 32 h + 31), and z = sum of phi(k).
+//   states:  one wave per (head, chunk, 32 x 32 tile (e, m)) of dS = phi(K)^T V over the
+//            chunk's 64 tokens, and z = sum of phi(k); operand columns staged in 8 KB of
+//            the wave's own LDS.
 //   outputs: wave w of a chunk owns query rows 32 (w & 1) ... + 31 and the value-column
-//            blocks w >> 1, (w >> 1) + 2, ...  It first forms A^T = phi(K) phi(Q)^T for
-//            the key blocks up to its own (the causal zero block is skipped; the diagonal
-//            block is masked).  In that layout a lane holds one query row and 16 keys,
-//            which are exactly the left operand of A V for those 16 keys, so A stays in
-//            registers; the normaliser's row sums are in-lane plus one exchange.
+//            blocks w >> 1, (w >> 1) + 2, ...  The chunk's three nonzero blocks of
+//            A^T = phi(K) phi(Q)^T (the causal zero block is skipped, the diagonal one
+//            masked) are formed once and shared through LDS.  In that layout a lane holds
+//            one query row and 16 keys, which are exactly the left operand of A V for
+//            those 16 keys, so A never returns to memory; the normaliser's row sums are
+//            in-lane plus one exchange.
 template <int E>
 struct LinChunkMfma {
     static constexpr int TC = 64, THREADS = 256, HE = E / 2;
@@ -543,6 +545,7 @@ struct LinChunkMfma {
     typedef __amdgpu_buffer_rsrc_t rsrc_t;
     static constexpr uint32_t kOff = 0x80000000u;  // an offset past every resource used here
     static __device__ __forceinline__ rsrc_t rsrc(const float *p, uint32_t bytes) {
+        // word 3: 32-bit data format, the setting for untyped (raw) buffer accesses on gfx9
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
     }
     static __device__ __forceinline__ float bload(rsrc_t r, uint32_t off) {
