@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void attn_linear_outputs_kernel(LinChunkArg
 // the half h = l / 32 of the terms in one contiguous run: its operands are 16-byte loads
 // of one row, straight from global memory into registers.
 //   states:  one wave per (head, chunk, 32 x 32 tile (e, m)) of dS = phi(K)^T V over the
-//            chunk's 64 tokens, and z = sum of phi(k); operand columns staged in 8 KB of
+//            chunk's 64 tokens, and z = sum of phi(k); operand columns staged in 4 KB of
 //            the wave's own LDS.
 //   outputs: wave w of a chunk owns query rows 32 (w & 1) ... + 31 and the value-column
 //            blocks w >> 1, (w >> 1) + 2, ...  The chunk's three nonzero blocks of
@@ -478,8 +478,8 @@ struct LinChunkMfma {
     // One wave per (head, chunk, tile (e block, m block)) of dS over the chunk's tokens.
     // The wave loads rows [c0, c0 + 64) x 32 columns of phi(K) and of V with 16-byte
     // loads (eight rows per load; zeros past the sequence end or the row), then stages
-    // them in LDS 32 tokens at a time (8 KB per wave, so LDS does not limit occupancy)
-    // and reads the operand columns from there.  Token of term (h, s) within a half is
+    // them in LDS 16 tokens at a time (4 KB per wave, so LDS does not limit occupancy)
+    // and reads the operand columns from there.  Token of term (h, s) within a part is
     // 2 s + h, so the two half-waves read adjacent LDS rows (distinct banks).
     static constexpr int STATE_TILES_PER_E = E / 32;
     static __device__ __forceinline__ void load_rows(f32x4_t (&val)[8], const float *src, int c0, int N, int W,
@@ -497,7 +497,7 @@ struct LinChunkMfma {
         }
     }
     static __device__ void states(const LinChunkArgs &a) {
-        __shared__ __attribute__((aligned(16))) float lds[2 * 32 * 32];
+        __shared__ __attribute__((aligned(16))) float lds[2 * 16 * 32];
         const int N = a.N, M = a.M;
         const bool fm = a.feature_map != 0;
         const int lane = threadIdx.x, col = lane & 31, h = lane >> 5, q = lane & 7, r0 = lane >> 3;
@@ -509,22 +509,22 @@ struct LinChunkMfma {
         const int bh = chunk / a.n_chunks, c = chunk - bh * a.n_chunks, c0 = c * TC;
         const int eb = tile / nm, mb = tile - eb * nm, e = 32 * eb + col, m = 32 * mb + col;
         float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
-        float *Ks = lds, *Vs = lds + 32 * 32;
+        float *Ks = lds, *Vs = lds + 16 * 32;
         f32x4_t kv4[8], vv4[8];
         load_rows(kv4, a.k + (size_t)bh * N * E, c0, N, E, 32 * eb, fm, lane);
         load_rows(vv4, a.v + (size_t)bh * N * M, c0, N, M, 32 * mb, false, lane);
         f32x16_t acc = {};
         float zs = 0.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // rows 32 half ... + 31 of the chunk are loads j = 4 half ... 4 half + 3
+        for (int part = 0; part < 4; ++part) {
+            // rows 16 part ... + 15 of the chunk are loads j = 2 part, 2 part + 1
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<f32x4_t *>(Ks + (r0 + 8 * j) * 32 + 4 * q) = kv4[4 * half + j];
-                *reinterpret_cast<f32x4_t *>(Vs + (r0 + 8 * j) * 32 + 4 * q) = vv4[4 * half + j];
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<f32x4_t *>(Ks + (r0 + 8 * j) * 32 + 4 * q) = kv4[2 * part + j];
+                *reinterpret_cast<f32x4_t *>(Vs + (r0 + 8 * j) * 32 + 4 * q) = vv4[2 * part + j];
             }
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
+            for (int s = 0; s < 8; ++s) {
                 const float kv = Ks[(2 * s + h) * 32 + col];
                 acc = mma(kv, Vs[(2 * s + h) * 32 + col], acc);
                 zs += kv;
@@ -646,13 +646,17 @@ struct LinChunkMfma {
     }
 };
 
+// six waves per SIMD (4 KB of LDS per wave)
 template <int E>
-__global__ __launch_bounds__(64) void attn_linear_states_mfma_kernel(LinChunkArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6)))
+void attn_linear_states_mfma_kernel(LinChunkArgs a) {
     LinChunkMfma<E>::states(a);
 }
 
+// up to E = 64 the output kernel fits four waves per SIMD without spilling
 template <int E>
-__global__ __launch_bounds__(256) void attn_linear_outputs_mfma_kernel(LinChunkArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E <= 64 ? 4 : 1)))
+void attn_linear_outputs_mfma_kernel(LinChunkArgs a) {
     LinChunkMfma<E>::outputs(a);
 }
 
