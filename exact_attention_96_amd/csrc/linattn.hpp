@@ -477,23 +477,26 @@ struct LinChunkMfma {
 
     // One wave per (head, chunk, tile (e block, m block)) of dS over the chunk's tokens.
     // The wave loads rows [c0, c0 + 64) x 32 columns of phi(K) and of V with 16-byte
-    // loads (eight rows per load; zeros past the sequence end or the row), then stages
-    // them in LDS 16 tokens at a time (4 KB per wave, so LDS does not limit occupancy)
+    // loads (eight rows per load; zeros past the sequence end or the row), 16 tokens at
+    // a time, and stages each part in LDS (4 KB per wave, so LDS does not limit occupancy)
     // and reads the operand columns from there.  Token of term (h, s) within a part is
     // 2 s + h, so the two half-waves read adjacent LDS rows (distinct banks).
     static constexpr int STATE_TILES_PER_E = E / 32;
-    static __device__ __forceinline__ void load_rows(f32x4_t (&val)[8], const float *src, int c0, int N, int W,
-                                                     int x0, bool fm, int lane) {
-        const int q = lane & 7, r0 = lane >> 3;
+    // rows t0 + 8 j (j = 0, 1) of phi(K) and V (one 16-token part of the chunk per lane group)
+    static __device__ __forceinline__ void load_part(f32x4_t (&kx)[2], f32x4_t (&vx)[2], const float *kh,
+                                                     const float *vh, int t0, int N, int M, int e0, int m0,
+                                                     bool fm, int q) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = c0 + r0 + 8 * j;
-            const bool ok = t < N && x0 + 4 * q < W;
-            val[j] = ok ? *reinterpret_cast<const f32x4_t *>(src + (size_t)t * W + x0 + 4 * q)
-                        : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + 8 * j;
+            const bool ok = t < N, okv = ok && m0 + 4 * q < M;
+            kx[j] = ok ? *reinterpret_cast<const f32x4_t *>(kh + (size_t)t * E + e0 + 4 * q)
+                       : (f32x4_t){0.f, 0.f, 0.f, 0.f};
             if (fm && ok)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) val[j][i] = phi(val[j][i]);
+                for (int i = 0; i < 4; ++i) kx[j][i] = phi(kx[j][i]);
+            vx[j] = okv ? *reinterpret_cast<const f32x4_t *>(vh + (size_t)t * M + m0 + 4 * q)
+                        : (f32x4_t){0.f, 0.f, 0.f, 0.f};
         }
     }
     static __device__ void states(const LinChunkArgs &a) {
@@ -510,19 +513,23 @@ struct LinChunkMfma {
         const int eb = tile / nm, mb = tile - eb * nm, e = 32 * eb + col, m = 32 * mb + col;
         float *W = a.ws + ((size_t)bh * a.n_chunks + c) * (size_t)(E * M + E);
         float *Ks = lds, *Vs = lds + 16 * 32;
-        f32x4_t kv4[8], vv4[8];
-        load_rows(kv4, a.k + (size_t)bh * N * E, c0, N, E, 32 * eb, fm, lane);
-        load_rows(vv4, a.v + (size_t)bh * N * M, c0, N, M, 32 * mb, false, lane);
+        const float *kh = a.k + (size_t)bh * N * E, *vh = a.v + (size_t)bh * N * M;
+        // two parts of 16 tokens in flight: part p + 2 is loaded once part p is in LDS
+        f32x4_t kb[2][2], vb[2][2];
+        load_part(kb[0], vb[0], kh, vh, c0 + r0, N, M, 32 * eb, 32 * mb, fm, q);
+        load_part(kb[1], vb[1], kh, vh, c0 + 16 + r0, N, M, 32 * eb, 32 * mb, fm, q);
         f32x16_t acc = {};
         float zs = 0.f;
 #pragma unroll
         for (int part = 0; part < 4; ++part) {
-            // rows 16 part ... + 15 of the chunk are loads j = 2 part, 2 part + 1
+            const int b = part & 1;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                *reinterpret_cast<f32x4_t *>(Ks + (r0 + 8 * j) * 32 + 4 * q) = kv4[2 * part + j];
-                *reinterpret_cast<f32x4_t *>(Vs + (r0 + 8 * j) * 32 + 4 * q) = vv4[2 * part + j];
+                *reinterpret_cast<f32x4_t *>(Ks + (r0 + 8 * j) * 32 + 4 * q) = kb[b][j];
+                *reinterpret_cast<f32x4_t *>(Vs + (r0 + 8 * j) * 32 + 4 * q) = vb[b][j];
             }
+            if (part + 2 < 4)
+                load_part(kb[b], vb[b], kh, vh, c0 + 16 * (part + 2) + r0, N, M, 32 * eb, 32 * mb, fm, q);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const float kv = Ks[(2 * s + h) * 32 + col];
@@ -646,9 +653,9 @@ struct LinChunkMfma {
     }
 };
 
-// six waves per SIMD (4 KB of LDS per wave)
+// seven waves per SIMD (4 KB of LDS per wave)
 template <int E>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(7)))
 void attn_linear_states_mfma_kernel(LinChunkArgs a) {
     LinChunkMfma<E>::states(a);
 }
