@@ -26,6 +26,7 @@ HIP_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    "-Werror",
     # never emit packed fp32 VALU ops (v_pk_add/mul/fma_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",

@@ -47,14 +47,16 @@
 // Otherwise (the first unit, or a row whose max grew well past m) the unit's row
 // max is taken, m moves to it, O~ and the row sum are rescaled and p is recomputed.
 // This changes no result: softmax is invariant to the shift (same page,
-// "数值稳定的 Softmax"), and p <= 2^16 keeps every intermediate far inside
-// fp32/bf16/fp16 range.  The row sum adds the fp32 probabilities before their
+// "数值稳定的 Softmax").  The bound keeps every p finite after its rounding for the
+// P V product: 2^16 for bf16 (8 exponent bits), 2^15 for fp16, whose largest finite
+// value is 65504 (a p in [65520, 65536] would round to inf).  The row sum adds the fp32 probabilities before their
 // rounding to the input type, so lse keeps fp32 accuracy (a sum of bf16-rounded
 // terms would cost ~2^-9 relative in l).
 #pragma once
 
 #include <type_traits>
 
+#include "addr.hpp"
 #include "common.hpp"
 
 namespace attn {
@@ -179,12 +181,13 @@ __device__ __forceinline__ void dma_to_lds16(const void *base, uint32_t voff, ui
 // The same with 4 bytes per lane (LDS at lds + 4 * lane).  base must be
 // wave-uniform; it is passed through readfirstlane so that it lives in SGPRs.
 __device__ __forceinline__ void dma_to_lds4(const void *base, uint32_t voff, uint32_t lds) {
-    // (readfirstlane returns a signed int: widen through uint32_t, or an address whose
-    // bit 31 is set would sign-extend into the upper word)
+    // (readfirstlane moves a signed int: the words are joined by addr_join, which widens
+    // them as unsigned; a sign-extended low word once faulted the GPU on a mask base with
+    // bit 31 set)
     const uint64_t b = reinterpret_cast<uintptr_t>(base);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t u = (uint64_t)lo | ((uint64_t)hi << 32);
+    const int lo = __builtin_amdgcn_readfirstlane(addr_lo_word(b));
+    const int hi = __builtin_amdgcn_readfirstlane(addr_hi_word(b));
+    const uint64_t u = addr_join(lo, hi);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
                  "s"(reinterpret_cast<const void *>(u)), "s"(lds)
                  : "memory", "m0");
@@ -226,7 +229,9 @@ struct MfmaFwd {
     static_assert(!MASK || MUNIT_B == NW * 64 * 4, "one 4-byte mask load per lane covers a unit");
     static constexpr int DB = D / 32;                // 32-row blocks of O^T
     static constexpr int DC = D / 16;                // k-steps of the first product
-    static constexpr float kSumBound = 65536.0f;  // 2^SUM_LOG2 with SUM_LOG2 = 16
+    // bound on a lane's fp32 sum of p for one unit, hence on every p: 2^16 for bf16; 2^15
+    // for fp16, so that no p rounds past fp16's largest finite value (65504)
+    static constexpr float kSumBound = std::is_same<T, _Float16>::value ? 32768.0f : 65536.0f;
     static_assert(LOADS >= 1 && LOADS * 64 * NW == BU * CH, "unit loads split evenly over the waves");
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
     static_assert(STAGES >= 3, "waits assume at least three ring stages");
