@@ -11,6 +11,7 @@
 #include "fwd_f32.hpp"
 #include "bwd_mfma.hpp"
 #include "fwd_mfma.hpp"
+#include "fwd_persist.hpp"
 #include "linattn.hpp"
 
 namespace {
@@ -72,6 +73,51 @@ hipError_t launch_mfma(const FwdArgs &a, int bh, hipStream_t stream) {
     return launch(&attn::attn_fwd_mfma_kernel<T, D, CAUSAL, MODE>, b.total, K::THREADS, lds_bytes, stream, b);
 }
 
+// Compute units of the current device (cached for devices 0..63).
+hipError_t device_cus(int *cus) {
+    static std::atomic<int> cache[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < 64;
+    if (tracked) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    if (tracked) cache[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return hipSuccess;
+}
+
+// The persistent kernel: one workgroup per compute unit (at most one per job), each
+// walking its list of jobs (pairs of causal query tiles, or single tiles).
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_persist(const FwdArgs &a, int bh, hipStream_t stream) {
+    typedef attn::MfmaFwdPersist<T, D, CAUSAL> K;
+    FwdArgs b = a;
+    b.n_qtiles = (a.Nq + K::BR - 1) / K::BR;
+    b.total = bh * b.n_qtiles;  // bounded by the check in fwd_core
+    b.p_nbh = bh;
+    b.p_jph = CAUSAL ? (b.n_qtiles + 1) / 2 : b.n_qtiles;
+    const long long jobs = (long long)bh * b.p_jph;
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const int grid = (int)(jobs < cus ? jobs : cus);
+    b.p_grid = grid;
+    b.p_xcd = (bh % 8 == 0 && grid % 8 == 0) ? 1 : 0;
+    e = opt_in_lds<K>(reinterpret_cast<const void *>(&attn::attn_fwd_persist_kernel<T, D, CAUSAL>), K::LDS_B);
+    if (e != hipSuccess) return e;
+    return launch(&attn::attn_fwd_persist_kernel<T, D, CAUSAL>, grid, K::THREADS, K::LDS_B, stream, b);
+}
+
 // MODE: attn::kFwdPlain / kFwdOffset / kFwdBits (the fp32 kernel only tells masked
 // from unmasked)
 template <int D, bool CAUSAL, int MODE>
@@ -88,6 +134,13 @@ hipError_t dispatch_dtype(const FwdArgs &a, int bh, int dtype, hipStream_t strea
 // everything else, including every equal-length problem, runs kFwdPlain.
 template <int D>
 hipError_t dispatch_mode(const FwdArgs &a, int bh, int causal, int dtype, hipStream_t stream) {
+    // equal lengths, no mask, 16-bit inputs, scale >= 0: the persistent kernel
+    if (!a.mask && a.Nq == a.Nk && dtype != ATTN_F32 && a.c >= 0.f) {
+        if (dtype == ATTN_F16)
+            return causal ? launch_persist<_Float16, D, true>(a, bh, stream)
+                          : launch_persist<_Float16, D, false>(a, bh, stream);
+        return causal ? launch_persist<__bf16, D, true>(a, bh, stream) : launch_persist<__bf16, D, false>(a, bh, stream);
+    }
     if (a.mask)
         return causal ? dispatch_dtype<D, true, attn::kFwdBits>(a, bh, dtype, stream)
                       : dispatch_dtype<D, false, attn::kFwdBits>(a, bh, dtype, stream);
@@ -245,6 +298,7 @@ int fwd_core(const void *q, const void *k, const void *v, const void *mask, cons
     a.tiles = static_cast<const uint64_t *>(tiles);
     a.tiles_w = (int)tw;
     a.tiles_nt = (int)nt;
+    a.p_grid = a.p_jph = a.p_nbh = a.p_xcd = 0;
     const int bh = B * H;
     const hipError_t err = d == 64 ? dispatch_mode<64>(a, bh, causal, dtype, stream)
                                    : dispatch_mode<128>(a, bh, causal, dtype, stream);

@@ -84,6 +84,9 @@ struct FwdArgs {
     // the tile sees a key of unit u (keys 64 u .. 64 u + 63).  NULL: no summary.
     const uint64_t *tiles;
     int tiles_w, tiles_nt;
+    // Persistent kernel only: grid size, jobs per head, heads, and whether the jobs of
+    // the heads congruent to x mod 8 go to the workgroups on XCD x.
+    int p_grid, p_jph, p_nbh, p_xcd;
 };
 
 // Query rows per tile of the mask summary (the matrix-core kernel's query tile).
@@ -255,7 +258,7 @@ struct MfmaFwd {
         uint32_t kaddr[DC];      // LDS address of this lane's K fragment for k-step cc (stage 0)
         uint32_t vaddr[DB];      // LDS address of this lane's V^T fragment for d block db (stage 0)
         float c;                 // scale * log2(e), >= 0
-        int r0, Nk, off, l32, g; // first row of the wave, key length, causal offset, lane coordinates
+        int r0, Nk, off;         // first row of the wave, key length, causal offset
         uint32_t mrow0;          // LDS address of the workgroup-relative row r0 in mask stage 0
                                  // (MASK; wave-uniform: the lane adds 8 * (lane % 32))
     };
@@ -328,14 +331,96 @@ struct MfmaFwd {
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // Variant used by the persistent kernel, which keeps fewer registers across a phase:
+    // the softmax phase reads only the first 32-key half of the next unit's K fragments
+    // (kload_half), and the matrix phase reads the second half itself, ahead of the V^T
+    // reads, while the score MFMAs of the first half run.  koff: LDS offset of the unit's
+    // K ring stage.
+    // These two take every fragment address from the k-step 0 and d-block 0 ones: under the
+    // swizzles above, the K fragment of k-step cc sits at kaddr[0] ^ (32 cc) and the V^T
+    // fragment of d block db at vaddr[0] ^ (64 db), so two registers hold what kaddr[] and
+    // vaddr[] hold.
+    // A ring stage offset (a multiple of 16 KB) commutes with these XORs (it only touches
+    // bits 14 and up), so a stage known only at run time costs one add per phase, not one
+    // per read.
+    // (a stage known at compile time stays an immediate offset of the reads)
+    static __device__ __forceinline__ uint32_t frag_addr(uint32_t base, uint32_t x, uint32_t off) {
+        if (__builtin_constant_p(off)) return (base ^ x) + off;
+        return (base + off) ^ x;
+    }
+    static __device__ __forceinline__ void kload_half(const State &S, KFrags &kf, uint32_t koff) {
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc)
+            kf[0][cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)(frag_addr(S.kaddr[0], (uint32_t)(cc << 5), koff)));
+    }
+    template <typename Dma>
+    static __device__ __forceinline__ void gemm_half(State &S, f32x16_t (&s)[2], const Packed &pk, KFrags &kf,
+                                                     uint32_t koff, uint32_t voff, Dma &&dma) {
+        // reads in issue order: while the first half's score MFMAs run, one K fragment of
+        // the second half and one V^T fragment half each (a fragment freed, one read in);
+        // then the remaining V^T reads, three per score MFMA of the second half
+        static_assert(UNIT_B % 16384 == 0 || UNIT_B == 8192, "stage offsets above the XOR'd address bits");
+        v8 vf[2][2][DB];
+        auto vread = [&](int n) {  // n-th transposing read: fragment n / 2, half n % 2
+            const int f = n >> 1, h = f / (2 * DB), kc = (f / DB) % 2, db = f % DB;
+            const uint32_t vb = frag_addr(S.vaddr[0], (uint32_t)(db << 6), voff) + h * 32 * ROWB + kc * 16 * ROWB + (n & 1) * 4 * ROWB;
+            const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(vb));
+            const u32x2_t x2 = __builtin_bit_cast(u32x2_t, x);
+            u32x4_t cur = __builtin_bit_cast(u32x4_t, vf[h][kc][db]);
+            if (n & 1) {
+                cur[2] = x2[0];
+                cur[3] = x2[1];
+            } else {
+                cur[0] = x2[0];
+                cur[1] = x2[1];
+            }
+            vf[h][kc][db] = as_v8(cur);
+        };
+        constexpr int NVR = 8 * DB;  // transposing reads per unit
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) {
+            kf[1][cc] = as_v8(*(const lds_u32x4_t *)(uintptr_t)(frag_addr(S.kaddr[0], (uint32_t)(cc << 5), koff) + 32 * ROWB));
+            vread(cc);
+        }
+#pragma unroll
+        for (int n = DC; n < NVR; ++n) vread(n);
+        s[0] = (f32x16_t){};
+        s[1] = (f32x16_t){};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) s[h] = M::mma(kf[h][cc], S.qf[cc], s[h]);
+        constexpr int NS = 2 * DC;  // score MFMAs per unit
+        sched_mfma_reads<DC, 2, 2 * DC>();
+        sched_mfma_reads<DC, (NVR - DC + DC - 1) / DC, NVR - DC>();
+        static_assert(NS == 2 * DC, "two halves of score MFMAs");
+        constexpr int NP = 4 * DB;       // P V MFMAs per unit
+        constexpr int CHUNK = NP / KVLOADS;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int h = j / (2 * DB), kc = (j / DB) % 2, db = j % DB;
+            const u32x4_t pp = {pk[h][kc][0], pk[h][kc][1], pk[h][kc][2], pk[h][kc][3]};
+            __builtin_amdgcn_sched_barrier(0);
+            S.acc[db] = M::mma(vf[h][kc][db], as_v8(pp), S.acc[db]);
+            if (j % CHUNK == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma(j / CHUNK);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
     // Keys of a unit are visible to this lane's row up to a per-lane limit:
     // accumulator register i of half h holds the key at offset key_off(h, i) from
     // the unit start k0, and that key is visible iff key_off(h, i) <= lim(k0), with
     // lim = min(row + off, Nk - 1) - k0 - 8 g (causal) or Nk - 1 - k0 - 8 g.
     static __device__ __forceinline__ constexpr int key_off(int h, int i) { return 32 * h + (i & 7) + 16 * (i >> 3); }
     static __device__ __forceinline__ int vis_limit(const State &S, int k0) {
-        const int last = CAUSAL ? min(S.r0 + S.l32 + S.off, S.Nk - 1) : S.Nk - 1;
-        return last - k0 - 8 * S.g;
+        // (lane coordinates from the lane id where used: nothing is kept live for them)
+        const uint32_t ln = lane_id_here();
+        const int l32 = (int)(ln & 31u), g = (int)(ln >> 5);
+        const int last = CAUSAL ? min(S.r0 + l32 + S.off, S.Nk - 1) : S.Nk - 1;
+        return last - k0 - 8 * g;
     }
 
     // MASK: visibility of the lane's 32 scores of a unit as bits, bit 16 h + i for
@@ -446,6 +531,53 @@ struct MfmaFwd {
         S.lsum += rs;
     }
 
+    // Epilogue of a wave's 32 rows r0 .. r0 + 31 of one head: O = O~ / l rounded to T,
+    // lse = (m + log2 l) ln 2 (fp32); a row that saw no key (l = 0, m = -inf) gets
+    // O = 0 and lse = -inf; rows at or past Nq are not stored.  o_head and lse_head
+    // point at the head's first row.  Register i of block b is output column
+    // 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q: the two lane halves of a row hold
+    // alternate groups of 4 columns.  For groups k and k + 1 of a block, one
+    // v_permlane32_swap per packed word (group k's word with group k + 1's) leaves lane
+    // half 0 with columns 8 k .. 8 k + 7 of its row and lane half 1 with columns
+    // 8 k + 8 .. 8 k + 15: one 16-byte store per lane and pair of groups.
+    static __device__ __forceinline__ void epilogue(const State &S, uint16_t *o_head, float *lse_head, int r0,
+                                                    int Nq, int lane_e) {
+        const int l32e = lane_e & 31, ge = lane_e >> 5;
+        const int q = r0 + l32e;
+        const float ltot = lane_swap32_add(S.lsum);
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        u32x4_t out[DB][2];
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {  // column groups k and k + 1 of block b
+                uint32_t w[2][2];             // [group k, k + 1][packed word]
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int i = 4 * (k + t);
+                    w[t][0] = M::pack(S.acc[b][i + 0] * inv, S.acc[b][i + 1] * inv);
+                    w[t][1] = M::pack(S.acc[b][i + 2] * inv, S.acc[b][i + 3] * inv);
+                }
+                const auto x0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+                const auto x1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+                out[b][k >> 1] = (u32x4_t){x0[0], x1[0], x0[1], x1[1]};
+            }
+        // (a head is below 2^31 bytes: 32-bit offset within it)
+        char *dst = reinterpret_cast<char *>(o_head) + ((uint32_t)q * (uint32_t)ROWB + (uint32_t)(16 * ge));
+        if (r0 + 32 <= Nq) {  // every row of the wave is stored (wave-uniform)
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) *reinterpret_cast<u32x4_t *>(dst + b * 64 + 32 * k) = out[b][k];
+        } else if (q < Nq) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) *reinterpret_cast<u32x4_t *>(dst + b * 64 + 32 * k) = out[b][k];
+        }
+        if (q < Nq && ge == 0) lse_head[q] = (S.m_ref + fast_log2(ltot)) * kLn2;
+    }
+
     // ------------------------------------------------------------ kernel body
 
     // Workgroup barrier after this wave's DMA has at most VMCNT loads in flight and
@@ -507,8 +639,6 @@ struct MfmaFwd {
         S.r0 = qt * BR + 64 * (w & 3) + 32 * (w >> 2);
         S.Nk = Nk;
         S.off = off;
-        S.l32 = l32;
-        S.g = g;
         // A negative scale is applied as -|c| by negating Q (exact), so c >= 0 below.
         S.c = a.c;
         uint32_t qsign = 0u;
@@ -847,44 +977,9 @@ struct MfmaFwd {
         // to this workgroup only while the workgroup runs.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-        // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2; a row that saw no key
-        // (l = 0, m = -inf) gets O = 0 and lse = -inf.  Register i of block b is
-        // output column 32 b + 8 (i >> 2) + 4 g + (i & 3) of row q, so the two lane halves
-        // of a row hold alternate groups of 4 columns.  One exchange between them (lane ^ 32,
-        // same row) gives every lane 8 consecutive columns: 16-byte stores, half as many
-        // store instructions as storing each lane's own groups of 4.
-        // (MASK: lane coordinates recomputed, so that they are not live across the loop)
-        const int lane_e = MASK ? (int)lane_id_here() : lane;
-        const int l32e = lane_e & 31, ge = lane_e >> 5;
-        const int q = S.r0 + l32e;
-        const float ltot = lane_swap32_add(S.lsum);
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        auto partner = [&](uint32_t x) -> uint32_t {  // x of lane ^ 32
-            const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-            return ge ? r[0] : r[1];
-        };
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int k = 0; k < 4; k += 2) {  // column groups 8 k .. 8 k + 15 of block b
-                u32x2_t mine[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int i = 4 * (k + t);
-                    mine[t][0] = M::pack(S.acc[b][i + 0] * inv, S.acc[b][i + 1] * inv);
-                    mine[t][1] = M::pack(S.acc[b][i + 2] * inv, S.acc[b][i + 3] * inv);
-                }
-                // lane half 0 keeps group k and receives the other half's group k; half 1
-                // keeps group k + 1 and receives the other half's group k + 1
-                const u32x2_t give = ge ? mine[0] : mine[1];
-                const u32x2_t got = {partner(give[0]), partner(give[1])};
-                const u32x2_t lo = ge ? got : mine[0], hi = ge ? mine[1] : got;
-                if (q < Nq) {
-                    uint16_t *dst = static_cast<uint16_t *>(a.o) + head + (size_t)q * D + b * 32 + 8 * (k + ge);
-                    *reinterpret_cast<u32x4_t *>(dst) = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
-                }
-            }
-        if (q < Nq && ge == 0) a.lse[(size_t)bh * Nq + q] = (S.m_ref + fast_log2(ltot)) * kLn2;
+        // ---- epilogue (MASK: lane id recomputed, so that it is not live across the loop)
+        epilogue(S, static_cast<uint16_t *>(a.o) + head, a.lse + (size_t)bh * Nq, S.r0, Nq,
+                 MASK ? (int)lane_id_here() : lane);
     }
 };
 
