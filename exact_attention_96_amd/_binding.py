@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ESCRATCH = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -43,6 +43,9 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float,
                                ci, ci, vp]
         L.attn_bwd.restype = ci
+        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, ci,
+                                       vp]
+        L.attn_bwd_noalloc.restype = ci
         ll = ctypes.c_longlong
         L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, ll, ll, vp, vp, ci, ci, ci, ci, ci,
                                       ctypes.c_float, ci, ci, vp]
@@ -156,6 +159,15 @@ def attn_bwd_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, d
     """Raw call with integer device addresses; returns the status code."""
     return int(lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d,
                               ctypes.c_float(scale), causal, dtype, stream))
+
+
+def attn_bwd_noalloc_ptr(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+                         B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+                         stream: int) -> int:
+    """Raw call of the no-allocation backward with integer device addresses; returns
+    the status code."""
+    return int(lib().attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d,
+                                      ctypes.c_float(scale), causal, dtype, stream))
 
 
 def _dtype_code(t) -> int:
@@ -337,7 +349,7 @@ def attn_fwd_masked(q, k, v, mask=None, causal: bool = False, scale: float | Non
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-             dq=None, dk=None, dv=None, delta=None):
+             dq=None, dk=None, dv=None, delta=None, noalloc: bool = False):
     """Attention backward on the GPU.
 
     q, k, v, o, dout: torch tensors [B, H, N, d] on one HIP device, one dtype
@@ -385,13 +397,30 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if not isinstance(lse, torch.Tensor):
         raise TypeError("lse must be a torch.Tensor")
     lse = _vec(lse, "lse")
-    delta = _vec(delta, "delta")
     dq, dk, dv = _like(dq, "dq"), _like(dk, "dk"), _like(dv, "dv")
+    if noalloc:
+        if delta is not None:
+            raise ValueError("the no-allocation backward takes no delta workspace")
+    else:
+        delta = _vec(delta, "delta")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                          delta.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code, stream)
+        if noalloc:
+            st = attn_bwd_noalloc_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                      B, H, N, d, float(scale), int(bool(causal)), code, stream)
+        else:
+            st = attn_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              delta.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), code, stream)
     if st != ATTN_OK:
-        raise AttnError(st, strerror(st), "attn_bwd")
+        raise AttnError(st, strerror(st), "attn_bwd_noalloc" if noalloc else "attn_bwd")
     return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = False, scale: float | None = None):
+    """attn_bwd through the entry point that allocates nothing (the per-row term D
+    lives in the library's fixed device scratch, B*H*N <= 2^22): for callers that
+    cannot allocate.  dq, dk, dv are the caller's output tensors (like q).  Calls
+    that overlap in time on one GPU race on that scratch."""
+    return attn_bwd(q, k, v, o, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv, noalloc=True)

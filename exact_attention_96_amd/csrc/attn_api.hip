@@ -344,10 +344,70 @@ extern "C" ATTN_API int attn_mask_pack(const void *mask, void *bits, void *tiles
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+namespace {
+
+// Checks and launches shared by attn_bwd and attn_bwd_noalloc.  delta: the caller's
+// workspace (checked against every other buffer) or, with own_delta, the library's
+// fixed scratch (nullptr here: it is looked up only after every check has passed).
+int bwd_core(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+             void *dq, void *dk, void *dv, float *delta, bool own_delta, int B, int H, int N, int d, float scale,
+             int causal, int dtype, hipStream_t stream);
+
+}  // namespace
+
 extern "C" ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                                  const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, int N,
                                  int d, float scale, int causal, int dtype, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
+    if (!delta) return ATTN_EINVAL;
+    return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, delta, false, B, H, N, d, scale, causal, dtype, stream);
+}
+
+namespace {
+
+// The scratch of attn_bwd_noalloc: D_i = dO_i . O_i for up to kScratchRows rows
+// (16 MiB of fp32), one copy per GPU for the life of the process.  Host code never
+// uses the symbol itself as an address: scratch_on_device() looks the device
+// address up once per device (with that device current) and keeps it.
+constexpr uint64_t kScratchRows = uint64_t(1) << 22;
+static __device__ __align__(256) float scratch[kScratchRows];
+
+hipError_t scratch_on_device(float **out) {
+    static std::atomic<float *> addr[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < 64;
+    if (tracked) {
+        float *p = addr[dev].load(std::memory_order_acquire);
+        if (p) {
+            *out = p;
+            return hipSuccess;
+        }
+    }
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    if (tracked) addr[dev].store(static_cast<float *>(p), std::memory_order_release);
+    *out = static_cast<float *>(p);
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" ATTN_API int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                                         const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                                         int H, int N, int d, float scale, int causal, int dtype,
+                                         hipStream_t stream) {
+    return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, nullptr, true, B, H, N, d, scale, causal, dtype, stream);
+}
+
+namespace {
+
+int bwd_core(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+             void *dq, void *dk, void *dv, float *delta, bool own_delta, int B, int H, int N, int d, float scale,
+             int causal, int dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
     if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
@@ -355,25 +415,32 @@ extern "C" ATTN_API int attn_bwd(const void *q, const void *k, const void *v, co
     const void *in16[] = {q, k, v, o, dout, dq, dk, dv};
     for (const void *p : in16)
         if (!aligned(p, 16)) return ATTN_EINVAL;
-    if (!aligned(lse, 4) || !aligned(delta, 4)) return ATTN_EINVAL;
+    if (!aligned(lse, 4) || (!own_delta && !aligned(delta, 4))) return ATTN_EINVAL;
     const uint64_t elt = dtype == ATTN_F32 ? 4 : 2;
     const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
     const uint64_t tb = rows * (uint64_t)d * elt, lb = rows * 4;
-    // each output against every input and every other output
+    // each output against every input and every other output (the library's own
+    // scratch overlaps nothing of the caller's)
     const void *outs[] = {dq, dk, dv, delta};
     const uint64_t out_b[] = {tb, tb, tb, lb};
+    const int n_outs = own_delta ? 3 : 4;
     const void *ins[] = {q, k, v, o, dout, lse};
     const uint64_t in_b[] = {tb, tb, tb, tb, tb, lb};
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < n_outs; ++i) {
         for (int j = 0; j < 6; ++j)
             if (overlaps(outs[i], out_b[i], ins[j], in_b[j])) return ATTN_EINVAL;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < n_outs; ++j)
             if (overlaps(outs[i], out_b[i], outs[j], out_b[j])) return ATTN_EINVAL;
     }
     if (dtype == ATTN_F32) return ATTN_EUNSUPPORTED;
     if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
     if ((uint64_t)B * (uint64_t)H * (((uint64_t)N + 127) / 128) > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
     if ((rows * (uint64_t)d / 8 + 255) / 256 > (uint64_t)INT32_MAX) return ATTN_EUNSUPPORTED;
+    if (own_delta) {
+        if (rows > kScratchRows) return ATTN_ESCRATCH;
+        const hipError_t e = scratch_on_device(&delta);
+        if (e != hipSuccess) return ATTN_EHIP;
+    }
 
     BwdArgs a;
     a.q = q;
@@ -396,6 +463,8 @@ extern "C" ATTN_API int attn_bwd(const void *q, const void *k, const void *v, co
                                    : bwd_causal<128>(a, bh, causal, dtype, stream);
     return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
+
+}  // namespace
 
 template <int E>
 hipError_t launch_linear(const attn::LinArgs &a, int grid, hipStream_t stream) {
@@ -536,6 +605,7 @@ extern "C" ATTN_API const char *attn_strerror(int status) {
         case ATTN_EINVAL: return "invalid argument";
         case ATTN_EUNSUPPORTED: return "unsupported head dimension or problem size";
         case ATTN_EHIP: return "HIP runtime error at launch";
+        case ATTN_ESCRATCH: return "problem larger than the fixed scratch of attn_bwd_noalloc (B*H*N above 2^22)";
         default: return "unknown status";
     }
 }

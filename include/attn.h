@@ -1,8 +1,9 @@
 /*
  * attn.h — C ABI of the exact attention library for MI355X (gfx950):
- * forward (attn_fwd), backward (attn_bwd), forward with unequal query/key
- * lengths and boolean masks (attn_fwd_masked, attn_mask_pack), and causal
- * linear attention (attn_linear_fwd, attn_linear_workspace_bytes).
+ * forward (attn_fwd), backward (attn_bwd, and attn_bwd_noalloc for callers that
+ * cannot allocate), forward with unequal query/key lengths and boolean masks
+ * (attn_fwd_masked, attn_mask_pack), and causal linear attention
+ * (attn_linear_fwd, attn_linear_workspace_bytes).
  *
  * The operation is exact scaled-dot-product attention, one (batch, head) at a
  * time:
@@ -48,11 +49,12 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,       /* invalid argument; nothing was launched */
     ATTN_EUNSUPPORTED = 2, /* valid but unsupported (head dim, size); nothing launched */
-    ATTN_EHIP = 3          /* the HIP runtime reported an error at launch */
+    ATTN_EHIP = 3,         /* the HIP runtime reported an error at launch */
+    ATTN_ESCRATCH = 4      /* attn_bwd_noalloc: B*H*N above its fixed scratch; nothing launched */
 } attn_status_t;
 
 /* Version of this ABI; bumped when entry points change or are added. */
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /*
  * attn_fwd — attention forward for B*H independent heads.
@@ -224,6 +226,29 @@ ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o
                       const float *lse, const void *dout, void *dq, void *dk, void *dv,
                       float *delta, int B, int H, int N, int d, float scale, int causal,
                       int dtype, hipStream_t stream);
+
+/*
+ * attn_bwd_noalloc — attn_bwd without the workspace argument, for callers that
+ * cannot allocate device memory (code being captured into a HIP graph, serving
+ * loops that must not call hipMalloc, harnesses that forbid it).
+ *
+ * Same operation, arguments (minus delta), arithmetic, results (bitwise those
+ * of attn_bwd on the same inputs) and errors as attn_bwd.  The per-row term
+ * D_i = dO_i . O_i lives in a scratch array that the library keeps in device
+ * memory for the life of the process, one copy per GPU, of 2^22 fp32 rows
+ * (16 MiB): B*H*N above 2^22 returns ATTN_ESCRATCH and launches nothing.  The
+ * call allocates nothing; its first call on a device looks up that device's
+ * copy (hipGetSymbolAddress) once.  Every row the call reads is written by the
+ * same call first, so nothing needs clearing between calls.
+ *
+ * Concurrency: all calls on one GPU share its scratch, so calls that may overlap
+ * in time on one GPU (different streams, or threads without ordering) race and
+ * give wrong gradients; serialise them (one stream, or events).
+ */
+ATTN_API int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                              int B, int H, int N, int d, float scale, int causal, int dtype,
+                              hipStream_t stream);
 
 /*
  * attn_linear_fwd — causal linear attention forward (fp32) for B*H independent

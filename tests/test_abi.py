@@ -19,7 +19,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_fwd", "attn_fwd_masked",
+    assert declared_symbols() == ["attn_abi_version", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_masked",
                                   "attn_linear_fwd", "attn_linear_workspace_bytes", "attn_mask_pack",
                                   "attn_strerror"]
 
@@ -49,6 +49,7 @@ def test_strerror():
     assert "invalid" in ea.strerror(1)
     assert "unsupported" in ea.strerror(2)
     assert "HIP" in ea.strerror(3)
+    assert "scratch" in ea.strerror(4)
     assert ea.strerror(12345) == "unknown status"
 
 
@@ -121,6 +122,35 @@ def test_bwd_invalid_arguments(kw):
                                 dict(B=65536, H=65536, N=1, d=64)])
 def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == ea.ATTN_EUNSUPPORTED
+
+
+NOALLOC_ORDER = [n for n in BWD_ORDER if n != "delta"]
+
+
+def call_bwd_noalloc(**kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return ea.attn_bwd_noalloc_ptr(*(a[n] for n in NOALLOC_ORDER))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(lse=0), dict(dout=0), dict(dq=0), dict(dv=0), dict(B=0), dict(d=0), dict(dtype=5),
+    dict(causal=3), dict(scale=float("inf")), dict(dk=DK + 8), dict(lse=L + 2), dict(dq=Q), dict(dv=DK),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_bwd_noalloc_invalid_arguments(kw):
+    assert call_bwd_noalloc(**kw) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(d=96), dict(B=65536, H=65536, N=1, d=64)])
+def test_bwd_noalloc_unsupported(kw):
+    assert call_bwd_noalloc(**kw) == ea.ATTN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("shape", [dict(B=1, H=1, N=(1 << 22) + 1), dict(B=2, H=64, N=32769),
+                                   dict(B=64, H=64, N=1025)])
+def test_bwd_noalloc_rejects_rows_beyond_its_scratch(shape):
+    """B*H*N above 2^22 rows: a status of its own, before any HIP call (CPU-safe)."""
+    assert call_bwd_noalloc(**shape) == ea.ATTN_ESCRATCH
 
 
 def test_bwd_outputs_right_after_inputs_are_fine():
