@@ -138,6 +138,78 @@ def summarize_traffic(args) -> None:
     print("\n".join(lines))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _smi_gfx_clocks():
+    """Current shader clocks (MHz, one per XCD) from amd-smi, or [] if unavailable."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if not exe:
+        return []
+    try:
+        out = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True,
+                             timeout=10).stdout
+        data = json.loads(out)
+    except (subprocess.SubprocessError, ValueError, OSError):
+        return []
+    gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+    clocks = []
+    for g in gpus if isinstance(gpus, list) else []:
+        for name, c in (g.get("clock") or {}).items():
+            if name.startswith("gfx_") and isinstance(c, dict):
+                v = (c.get("clk") or {}).get("value")
+                if isinstance(v, (int, float)):
+                    clocks.append(float(v))
+    return clocks
+
+
+def sustained_clock(step, seconds: float = 1.5):
+    """Median shader clock (MHz) over the XCDs, sampled with amd-smi while the same
+    step runs back to back for `seconds` right after the timed region (the timed region
+    itself is too short for the tool).  Returns a dict, or None without amd-smi."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            c = _smi_gfx_clocks()
+            if not c:
+                return
+            samples.append(c)
+
+    t = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    t.start()
+    while time.perf_counter() - t0 < seconds or (t.is_alive() and not samples and time.perf_counter() - t0 < 15):
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join(timeout=15)
+    if not samples:
+        return None
+    # readings below the lowest active DPM level (500 MHz) are an idle XCD between batches
+    flat = sorted(x for c in samples for x in c if x >= 500.0)
+    if not flat:
+        return None
+    return {"mhz_median": flat[len(flat) // 2], "mhz_min": flat[0], "mhz_max": flat[-1],
+            "samples": len(samples),
+            "source": "amd-smi metric --clock (per-XCD gfx clocks) polled while the step repeats for "
+                      f"{seconds:.1f} s right after the timed region"}
+
+
 def cpu_baseline(w, q, k, v, seconds: float):
     """The fp64 oracle (as it stands) on whole heads of the same workload, head after
     head until `seconds` of wall time have been spent (at least one head)."""
@@ -153,7 +225,7 @@ def cpu_baseline(w, q, k, v, seconds: float):
     dt = time.perf_counter() - t0
     flops = w.flops * done / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{done} of {w.B * w.H} heads, all {w.N} query rows each "
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
@@ -176,7 +248,7 @@ def cpu_baseline_bwd(w, q, k, v, do, seconds: float):
             break
     dt = time.perf_counter() - t0
     flops = 2.5 * w.flops * done / (w.B * w.H)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": T, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": T, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{done} of {w.B * w.H} heads, whole heads, {min(T, done)} at a time "
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
@@ -208,7 +280,7 @@ def cpu_baseline_masked(mw, q, k, v, mask, pairs: int, seconds: float):
     dt = time.perf_counter() - t0
     flops = 4.0 * mw.d * pairs * done
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{done} of {mw.B * mw.H} heads, all {mw.Nq} query rows each "
                       f"({flops:.3e} algorithmic flops in {dt:.1f} s)"}
 
@@ -238,6 +310,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle runs whole heads for cpu_baseline (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=None, help="(0: skip the cpu_baseline leg)")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="seconds of repeated steps while amd-smi samples the shader clock (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of this many bytes (counter calibration)")
     ap.add_argument("--summarize-traffic", action="store_true",
@@ -363,6 +437,15 @@ def main():
                      "kernel_ms_avg": round(avg_kernel_s * 1e3, 4),
                      "kernel_source_sha": kernel_source_hash()},
     }
+    if args.clock_seconds > 0 and w.dtype != "f32":
+        print(f"[bench] shader clock: amd-smi for ~{args.clock_seconds:.1f} s", file=sys.stderr, flush=True)
+        clk = sustained_clock(step, args.clock_seconds)
+        if clk is not None:
+            # the dense MFMA peak scales with the shader clock: 256 CU x clock x 4096 flop/clk
+            peak_at = PEAK_MFMA_BF16_TFLOPS * clk["mhz_median"] / 2400.0
+            clk["peak_at_clock_tflops"] = round(peak_at, 1)
+            clk["frac_at_clock"] = round(achieved / peak_at, 4)
+        out["roofline"]["sustained_clock"] = clk
     if args.cpu_seconds > 0 and args.cpu_heads != 0:
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds) if bwd else
@@ -386,6 +469,7 @@ def cpu_baseline_linear(lw, q, k, v, seconds: float):
     dt = time.perf_counter() - t0
     nbytes = lw.io_bytes * done / (lw.B * lw.H)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} of {lw.B * lw.H} heads, all {lw.N} tokens each "
                       f"({nbytes:.3e} algorithmic bytes in {dt:.1f} s; the oracle sums every "
                       f"key of every row, O(N^2) per head)"}
