@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <chrono>
+#include <random>
 #include <utility>
 
 #include "fwd_f32.hpp"
@@ -13,6 +15,7 @@
 #include "fwd_mfma.hpp"
 #include "fwd_persist.hpp"
 #include "linattn.hpp"
+#include "linscan.hpp"
 
 namespace {
 
@@ -519,10 +522,72 @@ int linear_chunk_lds_e(int M) {
 }
 int linear_chunk_lds(int E, int M) { return E == 16 ? linear_chunk_lds_e<16>(M) : 0; }
 
+// The one-pass kernel covers E, M in {32, 64}.
+bool linear_scan_shape(int E, int M) { return (E == 32 || E == 64) && (M == 32 || M == 64); }
+
+template <int E, int M>
+typename attn::LinScan<E, M>::Layout linear_scan_layout_em(long long BH, int N) {
+    typedef attn::LinScan<E, M> K;
+    const long long S = ((long long)N + K::L - 1) / K::L, SG = (S + K::G - 1) / K::G;
+    return K::layout(BH, S, SG);
+}
+size_t linear_scan_bytes(long long BH, int N, int E, int M) {
+    if (E == 32) return M == 32 ? linear_scan_layout_em<32, 32>(BH, N).bytes : linear_scan_layout_em<32, 64>(BH, N).bytes;
+    return M == 32 ? linear_scan_layout_em<64, 32>(BH, N).bytes : linear_scan_layout_em<64, 64>(BH, N).bytes;
+}
+
 extern "C" ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M) {
     if (B < 1 || H < 1 || N < 1 || E < 1 || M < 1) return -1;
     const uint64_t chunks = ((uint64_t)N + attn::LinChunk<16>::TC - 1) / attn::LinChunk<16>::TC;
-    return (long long)((uint64_t)B * (uint64_t)H * chunks * ((uint64_t)E * (uint64_t)M + (uint64_t)E) * 4);
+    const uint64_t chunked = (uint64_t)B * (uint64_t)H * chunks * ((uint64_t)E * (uint64_t)M + (uint64_t)E) * 4;
+    if (!linear_scan_shape(E, M)) return (long long)chunked;
+    const uint64_t scan = linear_scan_bytes((long long)B * H, N, E, M);
+    return (long long)(scan > chunked ? scan : chunked);
+}
+
+// A fresh nonzero 64-bit flag value per call of the one-pass kernel: a counter from a
+// random start, so that flags left in a workspace by earlier calls (or by whatever the
+// memory held before) do not match.
+unsigned long long next_epoch() {
+    static std::atomic<unsigned long long> counter{[] {
+        std::random_device rd;
+        const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        return ((unsigned long long)rd() << 32 ^ (unsigned long long)rd()) ^ (t * 0x9e3779b97f4a7c15ull);
+    }()};
+    unsigned long long e;
+    do e = counter.fetch_add(1, std::memory_order_relaxed) + 1; while (e == 0);
+    return e;
+}
+
+template <int E, int M>
+hipError_t launch_linear_scan(const float *q, const float *k, const float *v, float *o, void *ws, int BH, int N,
+                              int feature_map, float eps, hipStream_t stream) {
+    typedef attn::LinScan<E, M> K;
+    struct ScanTag {};
+    const hipError_t e = opt_in_lds<std::pair<K, ScanTag>>(
+        reinterpret_cast<const void *>(&attn::attn_linear_scan_kernel<E, M>), K::LDS_B);
+    if (e != hipSuccess) return e;
+    const long long S = ((long long)N + K::L - 1) / K::L, SG = (S + K::G - 1) / K::G;
+    const typename K::Layout l = K::layout(BH, S, SG);
+    char *base = static_cast<char *>(ws);
+    attn::LinScanArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.flag_agg = reinterpret_cast<unsigned long long *>(base + l.flag_agg);
+    a.flag_incl = reinterpret_cast<unsigned long long *>(base + l.flag_incl);
+    a.agg = reinterpret_cast<float *>(base + l.agg);
+    a.incl = reinterpret_cast<float *>(base + l.incl);
+    a.epoch = next_epoch();
+    a.N = N;
+    a.BH = BH;
+    a.BHp = (BH + 7) / 8 * 8;
+    a.S = (int)S;
+    a.SG = (int)SG;
+    a.eps = eps;
+    a.feature_map = feature_map;
+    return launch(&attn::attn_linear_scan_kernel<E, M>, (int)((long long)a.BHp * S), K::THREADS, K::LDS_B, stream, a);
 }
 
 extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, float *o, int B, int H, int N,
@@ -549,6 +614,18 @@ extern "C" ATTN_API int attn_linear_fwd(const float *q, const float *k, const fl
     const uint64_t grid = (uint64_t)B * (uint64_t)H * (uint64_t)(M / 16);
     if (grid > (uint64_t)INT32_MAX || (uint64_t)N * (uint64_t)(E > M ? E : M) > (uint64_t)INT32_MAX)
         return ATTN_EUNSUPPORTED;
+    if (workspace && linear_scan_shape(E, M) && ((uint64_t)N + 256) * 64 * 4 < (1ull << 31) &&
+        ((uint64_t)B * H + 7) / 8 * 8 * (((uint64_t)N + 127) / 128) <= (uint64_t)INT32_MAX) {
+        const int bh = B * H;
+        hipError_t e;
+        if (E == 32)
+            e = M == 32 ? launch_linear_scan<32, 32>(q, k, v, o, workspace, bh, N, feature_map, eps, stream)
+                        : launch_linear_scan<32, 64>(q, k, v, o, workspace, bh, N, feature_map, eps, stream);
+        else
+            e = M == 32 ? launch_linear_scan<64, 32>(q, k, v, o, workspace, bh, N, feature_map, eps, stream)
+                        : launch_linear_scan<64, 64>(q, k, v, o, workspace, bh, N, feature_map, eps, stream);
+        return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+    }
     const uint64_t chunks = ((uint64_t)N + 63) / 64;
     // the matrix-core chunk kernels address a head's v and o, and a chunk's state, with
     // 32-bit byte offsets below 2^31 (rows up to one chunk past the end included)

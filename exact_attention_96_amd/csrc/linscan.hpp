@@ -1,0 +1,376 @@
+// Causal linear attention in one pass over the sequence (fp32, matrix cores).
+//
+// "hqwc.cn" notes on the fast-transformers linear attention kernels, sections
+// 0x1-0x2: o_j = phi(q_j) S_j / (phi(q_j) . z_j + eps), S_j = sum_{t<=j} phi(k_t)
+// v_t^T, z_j = sum_{t<=j} phi(k_t), with phi = elu + 1.  The page carries S along
+// the sequence one token at a time; here the sum over t <= j is split at blocks of
+// tokens, as in the chunked kernels of linattn.hpp, but all three steps of those
+// kernels (block states, their prefix, the outputs) run in one launch.
+//
+// One workgroup (4 waves) per (head, span of L = 128 tokens); wave w owns the
+// 32 tokens T0 = 128 j + 32 w ... of span j.
+//   1. Each wave forms, from its own rows of phi(Q), phi(K), V:
+//        the in-span part of its outputs: A^T = phi(K) phi(Q)^T on its 32 x 32
+//        diagonal block (masked to key <= query), then A V and the row sums of A;
+//        its block state phi(K)^T V and key sum, written to its LDS region.
+//   2. The span's aggregate (the four block states added in wave order) goes to the
+//      workspace with a flag, then the workgroup takes the prefix of every earlier
+//      span of the head, P_j, in a fixed order (below).
+//   3. In LDS, each wave's region is replaced by its exclusive prefix P_j + the
+//      states of the waves before it; each wave then adds phi(Q) (that prefix) to
+//      its outputs, divides by the normaliser and stores o.
+// Spans are grouped by G = 8.  The last span of each group also publishes its
+// inclusive prefix.  Span j of group g0 = j - j % G sums, always in this order,
+//   P_j = INCL_{g0 - 1} + AGG_{g0} + AGG_{g0 + 1} + ... + AGG_{j - 1},
+// so the result does not depend on timing (the run is bitwise repeatable), a span
+// reads at most G aggregates, and the chain of inclusive prefixes has one link per
+// group instead of one per span.
+//
+// Workgroup b runs (head b % BHp, span b / BHp) with BHp a multiple of 8: every
+// span of a head is on the same XCD (workgroups go to the XCDs round robin), and
+// a span only waits for spans with a smaller index, which were dispatched before it.
+// A wait that has not ended after 2^18 polls (well under a second) gives up and marks
+// the outputs NaN rather than hang.
+//
+// The exchange goes through device-coherent accesses: the aggregates and prefixes
+// are stored with device-scope stores (write-through), the storing threads wait for
+// their completion (vmcnt) before the workgroup barrier after which one thread
+// writes the flag, and readers load the flag and then the data with device-scope
+// loads.  A flag holds the call's epoch (a 64-bit value the host takes fresh for
+// each call), so the workspace needs no clearing between calls.
+//
+// MFMA layouts (v_mfma_f32_32x32x2_f32: lane l gives row l % 32 of the left operand
+// and column l % 32 of the right one, at term l / 32; it keeps column l % 32, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 of register r).  Any sum may take its terms in any
+// order, so term (r, h) of a 16-step product is index 8 (r / 4) + 4 h + r % 4:
+// exactly the row that half h holds in register r of an accumulator.  Hence an
+// accumulator is already a right operand of the next product (A^T for A V, the
+// prefix state for phi(Q) S), with no data movement.
+#pragma once
+
+#include "common.hpp"
+
+namespace attn {
+
+struct LinScanArgs {
+    const float *q, *k, *v;
+    float *o;
+    unsigned long long *flag_agg, *flag_incl;  // [BH][S], [BH][SG]
+    float *agg, *incl;                          // [BH][S][ENT], [BH][SG][ENT]
+    unsigned long long epoch;                   // this call's flag value (nonzero)
+    int N, BH, BHp, S, SG;                      // S spans per head, SG groups of G spans
+    float eps;
+    int feature_map;
+};
+
+template <int E, int M>
+struct LinScan {
+    static constexpr int L = 128, TS = 32, NW = 4, THREADS = NW * 64, G = 8;
+    static constexpr int EB = E / 32, MB = M / 32;
+    // LDS row of a state (floats): the two lane halves write rows e and e + 4 at once,
+    // 4 MP floats apart, which the padding puts on the other 32 banks
+    static constexpr int MP = M + 8;
+    static constexpr int REG = E * MP + E;  // one wave's region: state rows, then key sum
+    static constexpr int ENT = E * M + E;   // entries of a state and key sum
+    static constexpr int PER = (ENT + THREADS - 1) / THREADS;
+    static constexpr int LDS_B = NW * REG * 4;
+    static constexpr int kSpins = 1 << 18;
+    static constexpr int kSc1 = 16;  // cache-policy bit of a buffer access: device scope
+    static_assert((E == 32 || E == 64) && (M == 32 || M == 64), "E, M in {32, 64}");
+    static_assert(2 * LDS_B <= 160 * 1024, "two workgroups per CU");
+
+    typedef __amdgpu_buffer_rsrc_t rsrc_t;
+    static __device__ __forceinline__ rsrc_t rsrc(const float *p, uint32_t bytes) {
+        // word 3: 32-bit data format, the setting for untyped (raw) buffer accesses on gfx9
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
+    }
+    // raw buffer accesses: an offset at or past the resource's size reads 0 / drops the store
+    static __device__ __forceinline__ float ld(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ f32x4_t ld4(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ void st(rsrc_t r, uint32_t off, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
+    }
+    // phi(x) = elu(x) + 1: x + 1 for x > 0, else e^x, here in five operations: x log2(e)
+    // as th + tl (a two-part constant; tl holds the rounding of x c_hi and the constant's
+    // tail), 2^th from v_exp_f32, times (1 + tl ln 2).  Measured on gfx950 against fp64 exp
+    // over x in [-87, 0]: at most 1.26 ulp (the library expf: 0.85 ulp, at three times
+    // the cost); results below the normal range flush to 0.
+    static __device__ __forceinline__ float phi(float x) {
+        const float c_hi = 1.44269502162933349609375f;  // log2(e) rounded to float
+        const float c_lo = 1.92596298909109e-8f;        // log2(e) - c_hi
+        const float th = x * c_hi;
+        const float tl = fmaf(x, c_hi, -th) + x * c_lo;
+        const float e = __builtin_amdgcn_exp2f(th);
+        return x > 0.f ? x + 1.f : fmaf(e, tl * 0.69314718055994530942f, e);
+    }
+    static __device__ __forceinline__ f32x16_t mma(float a, float b, const f32x16_t &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // LDS offset (floats, within a region) of state entry x: rows e of M values, then z
+    static __device__ __forceinline__ int lds_of(int x) {
+        return x < E * M ? (x / M) * MP + x % M : E * MP + (x - E * M);
+    }
+    static __device__ __forceinline__ rsrc_t rsrc_u64(const unsigned long long *p, int n) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned long long *>(p), (short)0, n * 8, 0x00020000);
+    }
+    // flag i of a resource, loaded device-coherently (sc1)
+    static __device__ __forceinline__ unsigned long long ld_flag(rsrc_t r, int i) {
+        return __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, i * 8, 0, kSc1));
+    }
+    static __device__ __forceinline__ float ld_dev(const float *p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    static __device__ __forceinline__ void st_dev(float *p, float x) {
+        __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every thread's device-scope stores are complete, then one thread raises the flag
+    static __device__ __forceinline__ void publish(unsigned long long *f, unsigned long long ep) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(f, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    static __device__ void run(const LinScanArgs &a) {
+        extern __shared__ __attribute__((aligned(16))) float lds[];
+        const int b = blockIdx.x, hh = b % a.BHp, j = b / a.BHp;
+        if (hh >= a.BH) return;  // padding of BH up to a multiple of 8
+        const int N = a.N;
+        const bool fm = a.feature_map != 0;
+        const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+        const int T0 = j * L + TS * w;
+        // the head's tensors (the host keeps each below 2^31 bytes, one span past the end included)
+        const rsrc_t rq = rsrc(a.q + (size_t)hh * N * E, (uint32_t)N * E * 4);
+        const rsrc_t rk = rsrc(a.k + (size_t)hh * N * E, (uint32_t)N * E * 4);
+        const rsrc_t rv = rsrc(a.v + (size_t)hh * N * M, (uint32_t)N * M * 4);
+        const rsrc_t ro = rsrc(a.o + (size_t)hh * N * M, (uint32_t)N * M * 4);
+
+        // ---- 1. this wave's block: loads (rows past N read 0)
+        // qf, kf: row T0 + c, terms e = 32 eb + 8 i + 4 h + u  ->  [16 eb + 4 i + u]
+        // vf: V[T0 + tok(r)][32 mb + c], kt: phi(K)[T0 + tok(r)][32 eb + c], tok(r) = 8 (r / 4) + 4 h + r % 4
+        float qf[EB * 16], kf[EB * 16], kt[EB * 16], vf[MB * 16];
+        {
+            const uint32_t row = (uint32_t)(T0 + c) * (E * 4);
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t off = row + (uint32_t)(32 * eb + 8 * i + 4 * h) * 4;
+                    const f32x4_t x = ld4(rq, off), y = ld4(rk, off);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        qf[16 * eb + 4 * i + u] = x[u];
+                        kf[16 * eb + 4 * i + u] = y[u];
+                    }
+                }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t tok = (uint32_t)(T0 + 8 * (r >> 2) + 4 * h + (r & 3));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) vf[16 * mb + r] = ld(rv, (tok * M + 32 * mb + c) * 4);
+#pragma unroll
+                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = ld(rk, (tok * E + 32 * eb + c) * 4);
+            }
+        }
+        if (fm) {
+#pragma unroll
+            for (int i = 0; i < EB * 16; ++i) {
+                qf[i] = phi(qf[i]);
+                kf[i] = phi(kf[i]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N;  // phi(0) = 1: keys past N stay 0
+#pragma unroll
+                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = in ? phi(kt[16 * eb + r]) : 0.f;
+            }
+        }
+
+        // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
+        f32x16_t at = {};
+#pragma unroll
+        for (int i = 0; i < EB * 16; ++i) at = mma(kf[i], qf[i], at);
+        float rs = 0.f;  // row sum of A for query T0 + c (keys up to the query)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            at[r] = 8 * (r >> 2) + 4 * h + (r & 3) > c ? 0.f : at[r];
+            rs += at[r];
+        }
+        rs += __shfl_xor(rs, 32);
+        // in-span outputs A V: lane = column 32 mb + c, register r = query T0 + tok(r)
+        f32x16_t ov[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            ov[mb] = (f32x16_t){};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ov[mb] = mma(at[r], vf[16 * mb + r], ov[mb]);
+        }
+        // block state phi(K)^T V and key sum into this wave's region
+        float *reg = lds + w * REG;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f32x16_t d = {};
+#pragma unroll
+                for (int r = 0; r < 16; ++r) d = mma(kt[16 * eb + r], vf[16 * mb + r], d);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    reg[(32 * eb + 8 * (r >> 2) + 4 * h + (r & 3)) * MP + 32 * mb + c] = d[r];
+            }
+            float zs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zs += kt[16 * eb + r];
+            zs += __shfl_xor(zs, 32);
+            if (h == 0) reg[E * MP + 32 * eb + c] = zs;
+        }
+        __syncthreads();
+
+        // ---- 2. the span's aggregate, then the prefix of the earlier spans
+        const int jg = j % G, g0 = j - jg;
+        const bool last = j == a.S - 1;
+        float ag[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int x = tid + i * THREADS;
+            ag[i] = 0.f;
+            if (x < ENT) {
+                const int o = lds_of(x);
+                ag[i] = ((lds[o] + lds[REG + o]) + lds[2 * REG + o]) + lds[3 * REG + o];
+            }
+        }
+        if (jg != G - 1 && !last) {  // read by the later spans of the group
+            float *dst = a.agg + ((size_t)hh * a.S + j) * ENT;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (tid + i * THREADS < ENT) st_dev(dst + tid + i * THREADS, ag[i]);
+            publish(a.flag_agg + (size_t)hh * a.S + j, a.epoch);
+        }
+        // every flag this span needs (the previous group's inclusive prefix, the earlier
+        // spans of its own group) is polled together, then all their data is loaded at
+        // once and added in the fixed order
+        bool ok = true;
+        if (j > 0) {
+            // device-scope (sc1) loads through buffer resources, so that the polls of one
+            // round are all in flight together; the compiler barrier makes every round load
+            // again
+            const rsrc_t fa = rsrc_u64(a.flag_agg + (size_t)hh * a.S, a.S);
+            const rsrc_t fi = rsrc_u64(a.flag_incl + (size_t)hh * a.SG, a.SG);
+            ok = false;
+            for (int it = 0; it < kSpins && !ok; ++it) {
+                asm volatile("" ::: "memory");
+                // (unconditional loads; an index past a resource, the previous group's for
+                // g0 = 0 included, reads 0 and is not used)
+                unsigned long long f[G];
+#pragma unroll
+                for (int u = 0; u < G; ++u) f[u] = ld_flag(fa, g0 + u);
+                const unsigned long long fg = ld_flag(fi, g0 / G - 1);
+                bool all = g0 == 0 || fg == a.epoch;
+#pragma unroll
+                for (int u = 0; u < G; ++u) all &= g0 + u >= j || f[u] == a.epoch;
+                ok = all;
+                if (!ok) __builtin_amdgcn_s_sleep(4);
+            }
+            asm volatile("" ::: "memory");  // the data loads stay after the flags
+        }
+        float pr[PER];
+        {
+            const float *src = a.incl + ((size_t)hh * a.SG + (g0 / G - 1)) * ENT + tid;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                pr[i] = g0 > 0 && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
+        }
+        for (int k0 = g0; k0 < j; k0 += 4) {  // up to four aggregates in flight
+            float t[4][PER];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float *src = a.agg + ((size_t)hh * a.S + k0 + u) * ENT + tid;
+#pragma unroll
+                for (int i = 0; i < PER; ++i)
+                    t[u][i] = k0 + u < j && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < PER; ++i)
+                    if (k0 + u < j) pr[i] += t[u][i];
+        }
+        if (!ok)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) pr[i] = __builtin_nanf("");
+        // ---- 3. exclusive prefix of each wave's block, in place; the group's last span
+        // publishes its inclusive prefix
+        const bool pub_incl = jg == G - 1 && !last;
+        float *inc = a.incl + ((size_t)hh * a.SG + j / G) * ENT;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int x = tid + i * THREADS;
+            if (x < ENT) {
+                const int o = lds_of(x);
+                float run = pr[i];
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float t = lds[ww * REG + o];
+                    lds[ww * REG + o] = run;
+                    run += t;
+                }
+                if (pub_incl) st_dev(inc + x, run);
+            }
+        }
+        if (pub_incl) publish(a.flag_incl + (size_t)hh * a.SG + j / G, a.epoch);
+        __syncthreads();
+
+        // outputs: + phi(Q) (exclusive prefix), over e in the order of qf
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    ov[mb] = mma(qf[16 * eb + s], reg[(32 * eb + 8 * (s >> 2) + 4 * h + (s & 3)) * MP + 32 * mb + c], ov[mb]);
+        float inv = 1.f;
+        if (fm) {
+            float d = 0.f;
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int s = 0; s < 16; ++s) d = fmaf(qf[16 * eb + s], reg[E * MP + 32 * eb + 8 * (s >> 2) + 4 * h + (s & 3)], d);
+            d += __shfl_xor(d, 32);
+            inv = 1.f / (d + rs + a.eps);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+                const float x = fm ? ov[mb][r] * __shfl(inv, row) : ov[mb][r];
+                st(ro, ((uint32_t)(T0 + row) * M + 32 * mb + c) * 4, x);
+            }
+    }
+
+    // workspace layout (bytes from the start; every part 256-byte aligned)
+    struct Layout {
+        size_t flag_agg, flag_incl, agg, incl, bytes;
+    };
+    static Layout layout(long long BH, long long S, long long SG) {
+        auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        Layout l;
+        l.flag_agg = 0;
+        l.flag_incl = up(l.flag_agg + (size_t)BH * S * 8);
+        l.agg = up(l.flag_incl + (size_t)BH * SG * 8);
+        l.incl = up(l.agg + (size_t)BH * S * ENT * 4);
+        l.bytes = up(l.incl + (size_t)BH * SG * ENT * 4);
+        return l;
+    }
+};
+
+template <int E, int M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_linear_scan_kernel(LinScanArgs a) {
+    LinScan<E, M>::run(a);
+}
+
+}  // namespace attn

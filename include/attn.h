@@ -274,20 +274,27 @@ ATTN_API int attn_bwd_noalloc(const void *q, const void *k, const void *v, const
  *   eps      finite, >= 0 (used with feature_map = 1; the page's default 1e-6).
  *   workspace  NULL, or device memory of at least attn_linear_workspace_bytes(B,
  *            H, N, E, M) bytes, 16-byte aligned, owned by the caller, overwritten
- *            (it must not overlap q, k, v or o).  With it the sequence is split
- *            into chunks of 64 tokens: per chunk phi(K)^T V and the key sum go to
- *            the workspace, an exclusive prefix over the chunks follows, and each
- *            chunk's outputs are phi(Q) times its prefix plus the causal
- *            in-chunk product (three launches, parallel over chunks; for E >= 32
- *            on the fp32 matrix cores).  Without it one sequential scan per
- *            (head, 16 value columns) runs instead; so it does where the chunk
- *            form's limits are exceeded: for E >= 32, (N + 128) * max(E, M) * 4
- *            and (E * M + E) * 4 below 2^31 bytes; for E = 16, tiles within LDS.
+ *            (it must not overlap q, k, v or o).  It needs no initialisation, and
+ *            calls that share one workspace must not overlap in time.  With it the
+ *            sum over t <= j is split at blocks of tokens, in one of two forms:
+ *            - E and M in {32, 64}: one launch; per span of 128 tokens, the
+ *              in-span products and the span's state (phi(K)^T V, key sum), then
+ *              the prefix of the earlier spans taken from the workspace in a fixed
+ *              order (spans publish their states there with flags), then
+ *              phi(Q) times the prefix (fp32 matrix cores);
+ *            - otherwise: chunks of 64 tokens in three launches: per chunk
+ *              phi(K)^T V and the key sum into the workspace, an exclusive prefix
+ *              over the chunks, then each chunk's outputs (for E >= 32 on the fp32
+ *              matrix cores).
+ *            Without a workspace one sequential scan per (head, 16 value columns)
+ *            runs instead; so it does where a block form's limits are exceeded:
+ *            for E >= 32, (N + 256) * max(E, M) * 4 and (E * M + E) * 4 below
+ *            2^31 bytes; for E = 16, tiles within LDS.
  *   workspace_bytes  size of workspace in bytes (ignored when it is NULL).
  *   stream   HIP stream the work is enqueued on.
  *
  * Arithmetic: fp32 throughout; the scan carries the state in token order, the
- * chunked form sums per chunk then over chunks (results of the two forms differ by
+ * block forms sum per block then over blocks (results of the forms differ by
  * rounding).  Results of one form are bitwise reproducible from call to call.
  * Ownership: as attn_fwd; o must not overlap q, k or v.
  * Errors (synchronous, nothing launched): ATTN_EINVAL (NULL pointer, a size < 1,
@@ -300,8 +307,11 @@ ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, flo
                              int H, int N, int E, int M, int feature_map, float eps,
                              void *workspace, long long workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace attn_linear_fwd's chunked form needs for these sizes
- * (B * H * ceil(N / 64) * (E * M + E) * 4), or -1 for a size < 1. */
+/* Bytes of workspace attn_linear_fwd's block forms need for these sizes, or -1
+ * for a size < 1: the larger of the chunked form's B * H * ceil(N / 64) *
+ * (E * M + E) * 4 and, for E and M in {32, 64}, the one-pass form's layout (per
+ * head, an 8-byte flag and an (E * M + E)-float state per span of 128 tokens,
+ * and the same per group of 8 spans; four parts, each rounded up to 256 bytes). */
 ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

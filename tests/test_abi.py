@@ -248,7 +248,30 @@ def test_linear_unsupported(kw):
     assert call_l(ws=0, **kw) == ea.ATTN_EUNSUPPORTED
 
 
+def _scan_workspace(BH, N, E, M):
+    """The one-pass form's layout (E, M in {32, 64}): per head, a flag and an aggregate
+    (state and key sum, E M + E floats) per span of 128 tokens, and a flag and an
+    inclusive prefix per group of 8 spans; four parts, each 256-byte aligned."""
+    up = lambda x: (x + 255) // 256 * 256
+    S = (N + 127) // 128
+    SG = (S + 7) // 8
+    ent = E * M + E
+    off = up(BH * S * 8)
+    off = up(off + BH * SG * 8)
+    off = up(off + BH * S * ent * 4)
+    return up(off + BH * SG * ent * 4)
+
+
 def test_linear_workspace_bytes():
-    assert ea.linear_workspace_bytes(2, 3, 100, 64, 64) == 2 * 3 * 2 * (64 * 64 + 64) * 4
+    # the larger of the chunked form's [B H][chunks of 64][E M + E] fp32 and, where it
+    # applies, the one-pass form's layout
+    chunked = 2 * 3 * 2 * (64 * 64 + 64) * 4
+    assert ea.linear_workspace_bytes(2, 3, 100, 64, 64) == max(chunked, _scan_workspace(6, 100, 64, 64))
+    assert _scan_workspace(6, 100, 64, 64) > chunked  # one span, its aggregate and prefix
+    big = 2 * 32 * 128 * (64 * 64 + 64) * 4
+    assert ea.linear_workspace_bytes(2, 32, 8192, 64, 64) == max(big, _scan_workspace(64, 8192, 64, 64)) == big
+    assert ea.linear_workspace_bytes(1, 2, 300, 32, 64) == max(1 * 2 * 5 * (32 * 64 + 32) * 4,
+                                                                _scan_workspace(2, 300, 32, 64))
     assert ea.linear_workspace_bytes(1, 1, 64, 16, 16) == 1 * 1 * 1 * (16 * 16 + 16) * 4
+    assert ea.linear_workspace_bytes(1, 1, 64, 128, 48) == 1 * 1 * 1 * (128 * 48 + 128) * 4
     assert ea.linear_workspace_bytes(0, 1, 64, 16, 16) == -1
