@@ -19,9 +19,10 @@ key lengths, a boolean mask packed once before timing), counted at 4*d flops per
 visible (query, key) pair.
 
 With --workload l1 a step is one call of attn_linear_fwd (causal linear
-attention, fp32; the chunked form: chunk states, prefix over chunks, outputs, on
-a workspace allocated before timing), bound by HBM: the value is algorithmic GB/s
-(read q, k, v and write o once) against the 8 TB/s peak.
+attention, fp32; with E = M = 64 the one-pass form: per 128-token span its own
+products and state, the prefix of the earlier spans through the workspace, the
+outputs; the workspace is allocated before timing), bound by HBM: the value is
+algorithmic GB/s (read q, k, v and write o once) against the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -98,24 +99,23 @@ def summarize_traffic(args) -> None:
     """Write the HBM traffic summary from two attention runs (FETCH_SIZE, WRITE_SIZE) and the
     same two counters on a plain device copy of known size (calibration)."""
     from exact_attention_96_amd.workloads import LINEAR_WORKLOADS, WORKLOADS
+    # the launches of one call of the entry point (a step), summed: one kernel for the
+    # forward and for the one-pass linear form, three for the chunked linear form
     if args.workload in LINEAR_WORKLOADS:
-        # the chunked form's launches of one call, summed
         w = LINEAR_WORKLOADS[args.workload]
         kern = "attn_linear_"
-        fetch_kib = _counter_step(args.fetch_csv, "FETCH_SIZE", kern)
-        write_kib = _counter_step(args.write_csv, "WRITE_SIZE", kern)
     else:
         w = WORKLOADS[args.workload]
-        kern = "attn_fwd_mfma_kernel" if w.dtype != "f32" else "attn_fwd_f32_kernel"
-        fetch_kib = _counter_avg(args.fetch_csv, "FETCH_SIZE", kern)
-        write_kib = _counter_avg(args.write_csv, "WRITE_SIZE", kern)
+        kern = "attn_fwd_"
+    fetch_kib = _counter_step(args.fetch_csv, "FETCH_SIZE", kern)
+    write_kib = _counter_step(args.write_csv, "WRITE_SIZE", kern)
     copy_fetch_kib = _counter_avg(args.copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
     copy_write_kib = _counter_avg(args.copy_write_csv, "WRITE_SIZE", "copyBuffer")
     fetch_factor = args.copy_bytes / (copy_fetch_kib * 1024)
     write_factor = args.copy_bytes / (copy_write_kib * 1024)
     hbm = fetch_kib * 1024 * fetch_factor + write_kib * 1024 * write_factor
     lines = [
-        f"# HBM traffic of {kern}{'* (every launch of one call)' if kern == 'attn_linear_' else ''} on {w.name}",
+        f"# HBM traffic of {kern}* (every launch of one call) on {w.name}",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (rocprofv3 --pmc, one counter per run),",
         "# scaled by the ratio of known bytes to counter bytes on a device copy of copy_bytes.",
         f"workload = {w.name}",

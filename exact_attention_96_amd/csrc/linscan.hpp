@@ -63,9 +63,9 @@ struct LinScanArgs {
     int feature_map;
 };
 
-template <int E, int M>
+template <int E, int M, int NW = 4>
 struct LinScan {
-    static constexpr int L = 128, TS = 32, NW = 4, THREADS = NW * 64, G = 8;
+    static constexpr int TS = 32, L = NW * TS, THREADS = NW * 64, G = 8;
     static constexpr int EB = E / 32, MB = M / 32;
     // LDS row of a state (floats): the two lane halves write rows e and e + 4 at once,
     // 4 MP floats apart, which the padding puts on the other 32 banks
@@ -74,10 +74,11 @@ struct LinScan {
     static constexpr int ENT = E * M + E;   // entries of a state and key sum
     static constexpr int PER = (ENT + THREADS - 1) / THREADS;
     static constexpr int LDS_B = NW * REG * 4;
+    static constexpr int NB = 68 / PER < 1 ? 1 : 68 / PER;  // aggregates loaded together (~68 registers)
     static constexpr int kSpins = 1 << 18;
     static constexpr int kSc1 = 16;  // cache-policy bit of a buffer access: device scope
     static_assert((E == 32 || E == 64) && (M == 32 || M == 64), "E, M in {32, 64}");
-    static_assert(2 * LDS_B <= 160 * 1024, "two workgroups per CU");
+    static_assert(8 / NW * LDS_B <= 160 * 1024, "LDS of the workgroups that fill a CU at two waves per SIMD");
 
     typedef __amdgpu_buffer_rsrc_t rsrc_t;
     static __device__ __forceinline__ rsrc_t rsrc(const float *p, uint32_t bytes) {
@@ -239,7 +240,8 @@ struct LinScan {
             ag[i] = 0.f;
             if (x < ENT) {
                 const int o = lds_of(x);
-                ag[i] = ((lds[o] + lds[REG + o]) + lds[2 * REG + o]) + lds[3 * REG + o];
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) ag[i] += lds[ww * REG + o];
             }
         }
         if (jg != G - 1 && !last) {  // read by the later spans of the group
@@ -283,17 +285,17 @@ struct LinScan {
             for (int i = 0; i < PER; ++i)
                 pr[i] = g0 > 0 && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
         }
-        for (int k0 = g0; k0 < j; k0 += 4) {  // up to four aggregates in flight
-            float t[4][PER];
+        for (int k0 = g0; k0 < j; k0 += NB) {  // NB aggregates in flight
+            float t[NB][PER];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NB; ++u) {
                 const float *src = a.agg + ((size_t)hh * a.S + k0 + u) * ENT + tid;
 #pragma unroll
                 for (int i = 0; i < PER; ++i)
                     t[u][i] = k0 + u < j && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < NB; ++u)
 #pragma unroll
                 for (int i = 0; i < PER; ++i)
                     if (k0 + u < j) pr[i] += t[u][i];
@@ -367,10 +369,10 @@ struct LinScan {
     }
 };
 
-template <int E, int M>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int E, int M, int NW = 4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_linear_scan_kernel(LinScanArgs a) {
-    LinScan<E, M>::run(a);
+    LinScan<E, M, NW>::run(a);
 }
 
 }  // namespace attn
