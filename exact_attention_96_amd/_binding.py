@@ -114,8 +114,10 @@ def attn_linear_fwd(q, k, v, feature_map: bool = True, eps: float = 1e-6, out=No
     q, k: [B, H, N, E]; v: [B, H, N, M]; float32, contiguous, one HIP device.
     feature_map=True: phi = elu + 1 on q and k and the normaliser 1 / (phi(q_j) .
     sum_{t<=j} phi(k_t) + eps); False: the causal dot product of q and k as given.
-    chunked=True runs the chunked form on a workspace (allocated here with torch unless
-    one is passed: a uint8 tensor of at least linear_workspace_bytes); False the scan.
+    chunked=True runs a block form on a workspace (allocated here with torch unless one
+    is passed: a uint8 tensor of at least linear_workspace_bytes, needing no
+    initialisation): the one-pass form for E and M in {32, 64}, the chunked form
+    otherwise; False the scan.
     Returns o [B, H, N, M] float32, enqueued on torch's current stream.
     """
     import torch

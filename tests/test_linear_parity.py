@@ -162,6 +162,42 @@ def test_full_size_workload(chunked):
         assert (err / bar).max() <= 1.0
 
 
+# One-pass form (E and M in {32, 64} with a workspace): spans of 128 tokens, groups of 8
+# spans; heads padded to a multiple of 8 on the grid.  These shapes cross groups (the
+# inclusive-prefix chain), end in a ragged span, and pad the heads.
+ONE_PASS = [(1, 3, 2500, 32, 64), (2, 5, 1100, 64, 32), (1, 1, 1025, 32, 32), (1, 2, 4096 + 7, 64, 64)]
+
+
+@pytest.mark.parametrize("fm", [False, True])
+@pytest.mark.parametrize("shape", ONE_PASS, ids=lambda s: "x".join(map(str, s)))
+def test_one_pass_spans_and_groups(shape, fm):
+    q, k, v = inputs(*shape, seed=sum(shape) + 3)
+    check(q, k, v, fm, 1e-6, f"one-pass {shape}", True)
+
+
+def test_one_pass_repeats_bitwise_and_ignores_stale_workspace():
+    """The look-back reads earlier spans in a fixed order, so repeated calls give the same
+    bits whatever their timing; a workspace left by another call (other sizes, other
+    epochs) or filled with arbitrary bytes gives the same result as a fresh one."""
+    B, H, N, E, M = 1, 3, 2500, 32, 64
+    q, k, v = (t.to(DEV) for t in inputs(B, H, N, E, M, seed=21))
+    n = ea.linear_workspace_bytes(B, H, N, E, M)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref = ea.attn_linear_fwd(q, k, v, workspace=ws).cpu()
+    for _ in range(3):
+        assert torch.equal(ea.attn_linear_fwd(q, k, v, workspace=ws).cpu(), ref)
+    # another problem on the same workspace, then this one again
+    q2, k2, v2 = (t.to(DEV) for t in inputs(2, 2, 900, E, M, seed=22))
+    ea.attn_linear_fwd(q2, k2, v2, workspace=ws[:ea.linear_workspace_bytes(2, 2, 900, E, M)])
+    assert torch.equal(ea.attn_linear_fwd(q, k, v, workspace=ws).cpu(), ref)
+    # arbitrary bytes
+    g = torch.Generator(device="cpu").manual_seed(5)
+    ws.copy_(torch.randint(0, 256, (n,), generator=g, dtype=torch.uint8).to(DEV))
+    assert torch.equal(ea.attn_linear_fwd(q, k, v, workspace=ws).cpu(), ref)
+    ws.fill_(0xFF)
+    assert torch.equal(ea.attn_linear_fwd(q, k, v, workspace=ws).cpu(), ref)
+
+
 def test_side_stream_and_caller_workspace():
     """Both forms on a side stream; the chunked one on a workspace the caller passes."""
     q, k, v = inputs(1, 2, 300, 32, 32, seed=13)
