@@ -95,11 +95,11 @@ struct LinScan {
     static __device__ __forceinline__ void st(rsrc_t r, uint32_t off, float x) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
     }
-    // phi(x) = elu(x) + 1: x + 1 for x > 0, else e^x, here in five operations: x log2(e)
-    // as th + tl (a two-part constant; tl holds the rounding of x c_hi and the constant's
-    // tail), 2^th from v_exp_f32, times (1 + tl ln 2).  Measured on gfx950 against fp64 exp
-    // over x in [-87, 0]: at most 1.26 ulp (the library expf: 0.85 ulp, at three times
-    // the cost); results below the normal range flush to 0.
+    // phi(x) = elu(x) + 1: x + 1 for x > 0, else e^x as x log2(e) = th + tl (a two-part
+    // constant; tl holds the rounding of x c_hi and the constant's tail), 2^th from
+    // v_exp_f32, times (1 + tl ln 2): a few operations instead of the library expf's
+    // range reduction.  Measured on gfx950 against fp64 exp over x in [-87, 0]: at most
+    // 1.26 ulp (the library expf: 0.85 ulp); results below the normal range flush to 0.
     static __device__ __forceinline__ float phi(float x) {
         const float c_hi = 1.44269502162933349609375f;  // log2(e) rounded to float
         const float c_lo = 1.92596298909109e-8f;        // log2(e) - c_hi
