@@ -311,7 +311,7 @@ ATTN_API int attn_linear_fwd(const float *q, const float *k, const float *v, flo
  * for a size < 1: the larger of the chunked form's B * H * ceil(N / 64) *
  * (E * M + E) * 4 and, for E and M in {32, 64}, the one-pass form's layout (per
  * head, an 8-byte flag and an (E * M + E)-float state per span of 128 tokens,
- * and the same per group of 8 spans; four parts, each rounded up to 256 bytes). */
+ * and the same per group of 4 spans; four parts, each rounded up to 256 bytes). */
 ATTN_API long long attn_linear_workspace_bytes(int B, int H, int N, int E, int M);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

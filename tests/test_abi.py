@@ -251,10 +251,10 @@ def test_linear_unsupported(kw):
 def _scan_workspace(BH, N, E, M):
     """The one-pass form's layout (E, M in {32, 64}): per head, a flag and an aggregate
     (state and key sum, E M + E floats) per span of 128 tokens, and a flag and an
-    inclusive prefix per group of 8 spans; four parts, each 256-byte aligned."""
+    inclusive prefix per group of 4 spans; four parts, each 256-byte aligned."""
     up = lambda x: (x + 255) // 256 * 256
     S = (N + 127) // 128
-    SG = (S + 7) // 8
+    SG = (S + 3) // 4
     ent = E * M + E
     off = up(BH * S * 8)
     off = up(off + BH * SG * 8)

@@ -162,7 +162,7 @@ def test_full_size_workload(chunked):
         assert (err / bar).max() <= 1.0
 
 
-# One-pass form (E and M in {32, 64} with a workspace): spans of 128 tokens, groups of 8
+# One-pass form (E and M in {32, 64} with a workspace): spans of 128 tokens, groups of 4
 # spans; heads padded to a multiple of 8 on the grid.  These shapes cross groups (the
 # inclusive-prefix chain), end in a ragged span, and pad the heads.
 ONE_PASS = [(1, 3, 2500, 32, 64), (2, 5, 1100, 64, 32), (1, 1, 1025, 32, 32), (1, 2, 4096 + 7, 64, 64)]
