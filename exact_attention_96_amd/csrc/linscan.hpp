@@ -9,12 +9,12 @@
 //
 // One workgroup (4 waves) per (head, span of L = 128 tokens); wave w owns the
 // 32 tokens T0 = 128 j + 32 w ... of span j.
-//   1. Each wave forms, from its own rows of phi(Q), phi(K), V:
-//        the in-span part of its outputs: A^T = phi(K) phi(Q)^T on its 32 x 32
-//        diagonal block (masked to key <= query), then A V and the row sums of A;
-//        its block state phi(K)^T V and key sum, written to its LDS region.
+//   1. Each wave forms, from its own rows of phi(Q), phi(K), V, its block state
+//      phi(K)^T V and key sum, written to its LDS region, and A^T = phi(K) phi(Q)^T on
+//      its 32 x 32 diagonal block (masked to key <= query) with the row sums of A.
 //   2. The span's aggregate (the four block states added in wave order) goes to the
-//      workspace with a flag, then the workgroup takes the prefix of every earlier
+//      workspace; while those stores complete, each wave forms the in-span part of its
+//      outputs, A V.  Then a flag, and the workgroup takes the prefix of every earlier
 //      span of the head, P_j, in a fixed order (below).
 //   3. In LDS, each wave's region is replaced by its exclusive prefix P_j + the
 //      states of the waves before it; each wave then adds phi(Q) (that prefix) to
@@ -33,7 +33,8 @@
 // A wait that has not ended after 2^18 polls (well under a second) gives up and marks
 // the outputs NaN rather than hang.
 //
-// The exchange goes through device-coherent accesses: the aggregates and prefixes
+// The exchange goes through device-coherent accesses, 16 bytes (4 consecutive
+// entries) per thread and access: the aggregates and prefixes
 // are stored with device-scope stores (write-through), the storing threads wait for
 // their completion (vmcnt) before the workgroup barrier after which one thread
 // writes the flag, and readers load the flag and then the data with device-scope
@@ -73,9 +74,11 @@ struct LinScan {
     static constexpr int MP = M + 8;
     static constexpr int REG = E * MP + E;  // one wave's region: state rows, then key sum
     static constexpr int ENT = E * M + E;   // entries of a state and key sum
-    static constexpr int PER = (ENT + THREADS - 1) / THREADS;
+    // a thread handles groups of 4 consecutive entries x4 = tid, tid + THREADS, ...
+    static constexpr int CH = ENT / 4, PER = (CH + THREADS - 1) / THREADS;
     static constexpr int LDS_B = NW * REG * 4;
-    static constexpr int NB = 68 / PER < 1 ? 1 : 68 / PER;  // aggregates loaded together (~68 registers)
+    static constexpr int NB = 17 / PER < 1 ? 1 : 17 / PER;  // aggregates loaded together (~68 registers)
+    static constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every resource here
     static constexpr int kSpins = 1 << 18;
     static constexpr int kSc1 = 16;  // cache-policy bit of a buffer access: device scope
     static_assert((E == 32 || E == 64) && (M == 32 || M == 64), "E, M in {32, 64}");
@@ -96,18 +99,37 @@ struct LinScan {
     static __device__ __forceinline__ void st(rsrc_t r, uint32_t off, float x) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
     }
+    // device-scope (sc1) 16-byte accesses: the stores write through, the loads are coherent
+    static __device__ __forceinline__ f32x4_t ld4_dev(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
+    }
+    static __device__ __forceinline__ void st4_dev(rsrc_t r, uint32_t off, f32x4_t x) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, (int)off, 0, kSc1);
+    }
     // phi(x) = elu(x) + 1: x + 1 for x > 0, else e^x as x log2(e) = th + tl (a two-part
     // constant; tl holds the rounding of x c_hi and the constant's tail), 2^th from
     // v_exp_f32, times (1 + tl ln 2): a few operations instead of the library expf's
     // range reduction.  Measured on gfx950 against fp64 exp over x in [-87, 0]: at most
     // 1.26 ulp (the library expf: 0.85 ulp); results below the normal range flush to 0.
+    // Written as e^min(x, 0) + max(x, 0) (the exponential of 0 is exactly 1, so x > 0
+    // still gets x + 1), with no branch: a conditional exponential compiles to a branch
+    // per element.  A NaN x gives NaN.
     static __device__ __forceinline__ float phi(float x) {
         const float c_hi = 1.44269502162933349609375f;  // log2(e) rounded to float
         const float c_lo = 1.92596298909109e-8f;        // log2(e) - c_hi
-        const float th = x * c_hi;
-        const float tl = fmaf(x, c_hi, -th) + x * c_lo;
+        const bool pos = x > 0.f;
+        const float xn = pos ? 0.f : x;
+        const float th = xn * c_hi;
+        const float tl = fmaf(xn, c_hi, -th) + xn * c_lo;
         const float e = __builtin_amdgcn_exp2f(th);
-        return x > 0.f ? x + 1.f : fmaf(e, tl * 0.69314718055994530942f, e);
+        return fmaf(e, tl * 0.69314718055994530942f, e) + (pos ? x : 0.f);
+    }
+    // lane id (0..63) computed where it is used (volatile: not hoisted, not shared with
+    // earlier uses)
+    static __device__ __forceinline__ uint32_t lane_now() {
+        uint32_t x;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+        return x;
     }
     static __device__ __forceinline__ f32x16_t mma(float a, float b, const f32x16_t &c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -116,18 +138,13 @@ struct LinScan {
     static __device__ __forceinline__ int lds_of(int x) {
         return x < E * M ? (x / M) * MP + x % M : E * MP + (x - E * M);
     }
+    static __device__ __forceinline__ f32x4_t &lds4(float *base, int o) { return *(f32x4_t *)(base + o); }
     static __device__ __forceinline__ rsrc_t rsrc_u64(const unsigned long long *p, int n) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned long long *>(p), (short)0, n * 8, 0x00020000);
     }
     // flag i of a resource, loaded device-coherently (sc1)
     static __device__ __forceinline__ unsigned long long ld_flag(rsrc_t r, int i) {
         return __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, i * 8, 0, kSc1));
-    }
-    static __device__ __forceinline__ float ld_dev(const float *p) {
-        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    static __device__ __forceinline__ void st_dev(float *p, float x) {
-        __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // every thread's device-scope stores are complete, then one thread raises the flag
     static __device__ __forceinline__ void publish(unsigned long long *f, unsigned long long ep) {
@@ -185,31 +202,13 @@ struct LinScan {
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const bool in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N;  // phi(0) = 1: keys past N stay 0
+                // phi(0) = 1: keys past N are zeroed (by a factor, not a branch around phi)
+                const float in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N ? 1.f : 0.f;
 #pragma unroll
-                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = in ? phi(kt[16 * eb + r]) : 0.f;
+                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = phi(kt[16 * eb + r]) * in;
             }
         }
 
-        // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
-        f32x16_t at = {};
-#pragma unroll
-        for (int i = 0; i < EB * 16; ++i) at = mma(kf[i], qf[i], at);
-        float rs = 0.f;  // row sum of A for query T0 + c (keys up to the query)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            at[r] = 8 * (r >> 2) + 4 * h + (r & 3) > c ? 0.f : at[r];
-            rs += at[r];
-        }
-        rs += __shfl_xor(rs, 32);
-        // in-span outputs A V: lane = column 32 mb + c, register r = query T0 + tok(r)
-        f32x16_t ov[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            ov[mb] = (f32x16_t){};
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ov[mb] = mma(at[r], vf[16 * mb + r], ov[mb]);
-        }
         // block state phi(K)^T V and key sum into this wave's region
         float *reg = lds + w * REG;
 #pragma unroll
@@ -229,29 +228,58 @@ struct LinScan {
             zs += __shfl_xor(zs, 32);
             if (h == 0) reg[E * MP + 32 * eb + c] = zs;
         }
+        // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
+        f32x16_t at = {};
+#pragma unroll
+        for (int i = 0; i < EB * 16; ++i) at = mma(kf[i], qf[i], at);
+        float rs = 0.f;  // row sum of A for query T0 + c (keys up to the query)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            at[r] = 8 * (r >> 2) + 4 * h + (r & 3) > c ? 0.f : at[r];
+            rs += at[r];
+        }
+        rs += __shfl_xor(rs, 32);
+        __builtin_amdgcn_sched_barrier(0);  // (the products above, before the wait for the other waves)
         __syncthreads();
 
         // ---- 2. the span's aggregate, then the prefix of the earlier spans
         const int jg = j % G, g0 = j - jg;
         const bool last = j == a.S - 1;
-        float ag[PER];
+        // the head's aggregates and inclusive prefixes; an offset of kOut reads 0 and
+        // drops a store (entry groups past ENT, slots that are not there)
+        const rsrc_t rag = rsrc(a.agg + (size_t)hh * a.S * ENT, (uint32_t)a.S * ENT * 4);
+        const rsrc_t rin = rsrc(a.incl + (size_t)hh * a.SG * ENT, (uint32_t)a.SG * ENT * 4);
+        f32x4_t ag[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int x = tid + i * THREADS;
-            ag[i] = 0.f;
-            if (x < ENT) {
-                const int o = lds_of(x);
+            const int x4 = tid + i * THREADS;
+            ag[i] = (f32x4_t){};
+            if (x4 < CH) {
+                const int o = lds_of(4 * x4);
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) ag[i] += lds[ww * REG + o];
+                for (int ww = 0; ww < NW; ++ww) ag[i] += lds4(lds, ww * REG + o);
             }
         }
-        if (jg != G - 1 && !last) {  // read by the later spans of the group
-            float *dst = a.agg + ((size_t)hh * a.S + j) * ENT;
+        // stored when the later spans of the group read it (else dropped: issuing the stores
+        // on every path keeps the compiler's count of memory operations in flight the same
+        // on all paths, so that later waits for loads do not also wait for these stores)
+        const bool pub_agg = jg != G - 1 && !last;
 #pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (tid + i * THREADS < ENT) st_dev(dst + tid + i * THREADS, ag[i]);
-            publish(a.flag_agg + (size_t)hh * a.S + j, a.epoch);
+        for (int i = 0; i < PER; ++i) {
+            const int x4 = tid + i * THREADS;
+            st4_dev(rag, pub_agg && x4 < CH ? (uint32_t)(j * ENT + 4 * x4) * 4 : kOut, ag[i]);
         }
+        // the in-span products below run while the stores complete
+        __builtin_amdgcn_sched_barrier(0);
+        // in-span outputs A V: lane = column 32 mb + c, register r = query T0 + tok(r)
+        f32x16_t ov[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            ov[mb] = (f32x16_t){};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ov[mb] = mma(at[r], vf[16 * mb + r], ov[mb]);
+        }
+        if (pub_agg) publish(a.flag_agg + (size_t)hh * a.S + j, a.epoch);
         // every flag this span needs (the previous group's inclusive prefix, the earlier
         // spans of its own group) is polled together, then all their data is loaded at
         // once and added in the fixed order
@@ -279,22 +307,21 @@ struct LinScan {
             }
             asm volatile("" ::: "memory");  // the data loads stay after the flags
         }
-        float pr[PER];
-        {
-            const float *src = a.incl + ((size_t)hh * a.SG + (g0 / G - 1)) * ENT + tid;
+        f32x4_t pr[PER];
 #pragma unroll
-            for (int i = 0; i < PER; ++i)
-                pr[i] = g0 > 0 && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
+        for (int i = 0; i < PER; ++i) {
+            const int x4 = tid + i * THREADS;
+            pr[i] = ld4_dev(rin, g0 > 0 && x4 < CH ? (uint32_t)((g0 / G - 1) * ENT + 4 * x4) * 4 : kOut);
         }
         for (int k0 = g0; k0 < j; k0 += NB) {  // NB aggregates in flight
-            float t[NB][PER];
+            f32x4_t t[NB][PER];
 #pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const float *src = a.agg + ((size_t)hh * a.S + k0 + u) * ENT + tid;
+            for (int u = 0; u < NB; ++u)
 #pragma unroll
-                for (int i = 0; i < PER; ++i)
-                    t[u][i] = k0 + u < j && tid + i * THREADS < ENT ? ld_dev(src + i * THREADS) : 0.f;
-            }
+                for (int i = 0; i < PER; ++i) {
+                    const int x4 = tid + i * THREADS;
+                    t[u][i] = ld4_dev(rag, k0 + u < j && x4 < CH ? (uint32_t)((k0 + u) * ENT + 4 * x4) * 4 : kOut);
+                }
 #pragma unroll
             for (int u = 0; u < NB; ++u)
 #pragma unroll
@@ -303,24 +330,23 @@ struct LinScan {
         }
         if (!ok)
 #pragma unroll
-            for (int i = 0; i < PER; ++i) pr[i] = __builtin_nanf("");
+            for (int i = 0; i < PER; ++i) pr[i] = (f32x4_t)__builtin_nanf("");
         // ---- 3. exclusive prefix of each wave's block, in place; the group's last span
         // publishes its inclusive prefix
         const bool pub_incl = jg == G - 1 && !last;
-        float *inc = a.incl + ((size_t)hh * a.SG + j / G) * ENT;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int x = tid + i * THREADS;
-            if (x < ENT) {
-                const int o = lds_of(x);
-                float run = pr[i];
+            const int x4 = tid + i * THREADS;
+            if (x4 < CH) {
+                const int o = lds_of(4 * x4);
+                f32x4_t run = pr[i];
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
-                    const float t = lds[ww * REG + o];
-                    lds[ww * REG + o] = run;
+                    const f32x4_t t = lds4(lds, ww * REG + o);
+                    lds4(lds, ww * REG + o) = run;
                     run += t;
                 }
-                if (pub_incl) st_dev(inc + x, run);
+                if (pub_incl) st4_dev(rin, (uint32_t)((j / G) * ENT + 4 * x4) * 4, run);
             }
         }
         if (pub_incl) publish(a.flag_incl + (size_t)hh * a.SG + j / G, a.epoch);
@@ -344,13 +370,17 @@ struct LinScan {
             d += __shfl_xor(d, 32);
             inv = 1.f / (d + rs + a.eps);
         }
+        // (store offsets from a lane id taken here, so that the compiler does not keep the
+        // load offsets of the start alive until now)
+        const uint32_t ln = lane_now(), oc = ln & 31, oh = ln >> 5;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 8 * (r >> 2) + 4 * h + (r & 3);
                 const float x = fm ? ov[mb][r] * __shfl(inv, row) : ov[mb][r];
-                st(ro, ((uint32_t)(T0 + row) * M + 32 * mb + c) * 4, x);
+                const uint32_t orow = (uint32_t)(T0 + 8 * (r >> 2) + (r & 3)) + 4 * oh;
+                st(ro, (orow * M + 32 * mb + oc) * 4, x);
             }
     }
 
