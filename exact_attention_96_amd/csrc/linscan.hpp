@@ -172,27 +172,30 @@ struct LinScan {
         // vf: V[T0 + tok(r)][32 mb + c], kt: phi(K)[T0 + tok(r)][32 eb + c], tok(r) = 8 (r / 4) + 4 h + r % 4
         float qf[EB * 16], kf[EB * 16], kt[EB * 16], vf[MB * 16];
         {
+            // in the order of use: K (for kt), V, then Q
             const uint32_t row = (uint32_t)(T0 + c) * (E * 4);
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t off = row + (uint32_t)(32 * eb + 8 * i + 4 * h) * 4;
-                    const f32x4_t x = ld4(rq, off), y = ld4(rk, off);
+                    const f32x4_t y = ld4(rk, row + (uint32_t)(32 * eb + 8 * i + 4 * h) * 4);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        qf[16 * eb + 4 * i + u] = x[u];
-                        kf[16 * eb + 4 * i + u] = y[u];
-                    }
+                    for (int u = 0; u < 4; ++u) kf[16 * eb + 4 * i + u] = y[u];
                 }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint32_t tok = (uint32_t)(T0 + 8 * (r >> 2) + 4 * h + (r & 3));
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) vf[16 * mb + r] = ld(rv, (tok * M + 32 * mb + c) * 4);
-#pragma unroll
-                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = ld(rk, (tok * E + 32 * eb + c) * 4);
             }
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t x = ld4(rq, row + (uint32_t)(32 * eb + 8 * i + 4 * h) * 4);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) qf[16 * eb + 4 * i + u] = x[u];
+                }
         }
         if (fm) {
 #pragma unroll
@@ -200,17 +203,31 @@ struct LinScan {
                 qf[i] = phi(qf[i]);
                 kf[i] = phi(kf[i]);
             }
+        }
+        float *reg = lds + w * REG;
+        {
+            // kt is kf transposed, through this wave's LDS region (free until its state is
+            // written): rows of KP floats, so that the two lane halves (rows 4 apart) read
+            // the two halves of the banks
+            constexpr int KP = E + 8;
+            static_assert(TS * KP <= REG, "the phi(K) block fits in a wave's region");
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds4(reg, c * KP + 32 * eb + 8 * i + 4 * h) =
+                        (f32x4_t){kf[16 * eb + 4 * i], kf[16 * eb + 4 * i + 1], kf[16 * eb + 4 * i + 2], kf[16 * eb + 4 * i + 3]};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                // phi(0) = 1: keys past N are zeroed (by a factor, not a branch around phi)
+                // phi(0) = 1: keys past N are zeroed
                 const float in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N ? 1.f : 0.f;
 #pragma unroll
-                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = phi(kt[16 * eb + r]) * in;
+                for (int eb = 0; eb < EB; ++eb)
+                    kt[16 * eb + r] = reg[(8 * (r >> 2) + 4 * h + (r & 3)) * KP + 32 * eb + c] * in;
             }
         }
 
         // block state phi(K)^T V and key sum into this wave's region
-        float *reg = lds + w * REG;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb) {
 #pragma unroll
