@@ -69,10 +69,13 @@ template <int E, int M, int NW = 4>
 struct LinScan {
     static constexpr int TS = 32, L = NW * TS, THREADS = NW * 64, G = 4;
     static constexpr int EB = E / 32, MB = M / 32;
-    // LDS row of a state (floats): the two lane halves write rows e and e + 4 at once,
-    // 4 MP floats apart, which the padding puts on the other 32 banks
-    static constexpr int MP = M + 8;
-    static constexpr int REG = E * MP + E;  // one wave's region: state rows, then key sum
+    // A state sits in LDS by value column: row m holds the E entries (e, m), EP floats
+    // apart, then the key sum.  A lane reads or writes 4 consecutive e of its column m
+    // at once, and the 16 lanes of one 16-byte LDS access (columns c .. c + 15) start 4
+    // banks apart.  The region also holds, before the state is written, the wave's phi(K)
+    // block (TS rows of E + 8 floats).
+    static constexpr int EP = E + 4;
+    static constexpr int REG = M * EP + E > TS * (E + 8) ? M * EP + E : TS * (E + 8);
     static constexpr int ENT = E * M + E;   // entries of a state and key sum
     // a thread handles groups of 4 consecutive entries x4 = tid, tid + THREADS, ...
     static constexpr int CH = ENT / 4, PER = (CH + THREADS - 1) / THREADS;
@@ -136,7 +139,7 @@ struct LinScan {
     }
     // LDS offset (floats, within a region) of state entry x: rows e of M values, then z
     static __device__ __forceinline__ int lds_of(int x) {
-        return x < E * M ? (x / M) * MP + x % M : E * MP + (x - E * M);
+        return x < E * M ? (x / E) * EP + x % E : M * EP + (x - E * M);
     }
     static __device__ __forceinline__ f32x4_t &lds4(float *base, int o) { return *(f32x4_t *)(base + o); }
     static __device__ __forceinline__ rsrc_t rsrc_u64(const unsigned long long *p, int n) {
@@ -236,14 +239,15 @@ struct LinScan {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) d = mma(kt[16 * eb + r], vf[16 * mb + r], d);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    reg[(32 * eb + 8 * (r >> 2) + 4 * h + (r & 3)) * MP + 32 * mb + c] = d[r];
+                for (int g = 0; g < 4; ++g)
+                    lds4(reg, (32 * mb + c) * EP + 32 * eb + 8 * g + 4 * h) =
+                        (f32x4_t){d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
             }
             float zs = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) zs += kt[16 * eb + r];
             zs += __shfl_xor(zs, 32);
-            if (h == 0) reg[E * MP + 32 * eb + c] = zs;
+            if (h == 0) reg[M * EP + 32 * eb + c] = zs;
         }
         // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
         f32x16_t at = {};
@@ -375,15 +379,22 @@ struct LinScan {
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-                for (int s = 0; s < 16; ++s)
-                    ov[mb] = mma(qf[16 * eb + s], reg[(32 * eb + 8 * (s >> 2) + 4 * h + (s & 3)) * MP + 32 * mb + c], ov[mb]);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4_t bv = lds4(reg, (32 * mb + c) * EP + 32 * eb + 8 * g + 4 * h);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) ov[mb] = mma(qf[16 * eb + 4 * g + t], bv[t], ov[mb]);
+                }
         float inv = 1.f;
         if (fm) {
             float d = 0.f;
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-                for (int s = 0; s < 16; ++s) d = fmaf(qf[16 * eb + s], reg[E * MP + 32 * eb + 8 * (s >> 2) + 4 * h + (s & 3)], d);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4_t zv = lds4(reg, M * EP + 32 * eb + 8 * g + 4 * h);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) d = fmaf(qf[16 * eb + 4 * g + t], zv[t], d);
+                }
             d += __shfl_xor(d, 32);
             inv = 1.f / (d + rs + a.eps);
         }
