@@ -1,4 +1,5 @@
-// Causal linear attention in one pass over the sequence (fp32, matrix cores).
+// Causal linear attention in one pass over the sequence (fp32 data; products on the
+// bf16 matrix cores from three-part splits, to fp32 accuracy).
 //
 // "hqwc.cn" notes on the fast-transformers linear attention kernels, sections
 // 0x1-0x2: o_j = phi(q_j) S_j / (phi(q_j) . z_j + eps), S_j = sum_{t<=j} phi(k_t)
@@ -41,13 +42,21 @@
 // loads.  A flag holds the call's epoch (a 64-bit value the host takes fresh for
 // each call), so the workspace needs no clearing between calls.
 //
-// MFMA layouts (v_mfma_f32_32x32x2_f32: lane l gives row l % 32 of the left operand
-// and column l % 32 of the right one, at term l / 32; it keeps column l % 32, rows
-// 8 (r / 4) + 4 (l / 32) + r % 4 of register r).  Any sum may take its terms in any
-// order, so term (r, h) of a 16-step product is index 8 (r / 4) + 4 h + r % 4:
-// exactly the row that half h holds in register r of an accumulator.  Hence an
-// accumulator is already a right operand of the next product (A^T for A V, the
-// prefix state for phi(Q) S), with no data movement.
+// Products.  Each 16-term piece of a product runs as six v_mfma_f32_32x32x16_bf16 on
+// three-part bf16 splits of its operands (x = h + m + l to within 2^-24 |x|; see
+// split8): each product is then within a few units of 2^-24 of its value and the sums
+// are fp32, so the results keep fp32-level accuracy at 2.7x the rate of
+// v_mfma_f32_32x32x2_f32 (6 x 32 cycles against 8 x 64 for 16 terms).
+//
+// MFMA layouts (32 x 32 x 16: lane l gives row l % 32 of the left operand and column
+// l % 32 of the right one, at terms 8 (l / 32) .. 8 (l / 32) + 7; it keeps column
+// l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4 of register r).  Any sum may take its
+// terms in any order, so term (i, h) of the 16-term piece kb may be index
+// tok(8 kb + i) = 8 ((8 kb + i) / 4) + 4 h + i % 4: exactly the row that half h holds
+// in register 8 kb + i of an accumulator.  Hence an accumulator is already an operand
+// of the next product (A^T for A V), with no data movement; the pieces over the state
+// width take, for half h, the e that the lane's rows of phi(Q) and phi(K) hold
+// (32 eb + 16 kk + 8 (j / 4) + 4 h + j % 4 for element j of piece (eb, kk)).
 #pragma once
 
 #include "common.hpp"
@@ -134,8 +143,46 @@ struct LinScan {
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
         return x;
     }
-    static __device__ __forceinline__ f32x16_t mma(float a, float b, const f32x16_t &c) {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    // Three-part bf16 split of 8 floats, for products on the bf16 matrix cores that keep
+    // fp32 accuracy: x = h + m + l + d with h = bf16(x), m = bf16(x - h), l = bf16(x - h - m)
+    // (nearest even; each difference exact in fp32), so |m| <= 2^-8 |x|, |l| <= 2^-16 |x|
+    // and |d| <= 2^-24 |x|.  The product x y then takes the six terms h h' + h m' + m h'
+    // + m m' + h l' + l h'; the terms left out, m l', l m' and l l', are at most 2^-24,
+    // 2^-24 and 2^-32 of |x y|.  Packed pairs: element 2 i in the low half of word i.
+    struct Split8 {
+        bf16x8_t h, m, l;
+    };
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+        const f32x2_t v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+    static __device__ __forceinline__ float lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+    static __device__ __forceinline__ float hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+    static __device__ __forceinline__ Split8 split8(const float *x) {
+        u32x4_t h, m, l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = x[2 * i], b = x[2 * i + 1];
+            h[i] = pk_bf16(a, b);
+            const float ra = a - lo_f(h[i]), rb = b - hi_f(h[i]);
+            m[i] = pk_bf16(ra, rb);
+            l[i] = pk_bf16(ra - lo_f(m[i]), rb - hi_f(m[i]));
+        }
+        return {__builtin_bit_cast(bf16x8_t, h), __builtin_bit_cast(bf16x8_t, m), __builtin_bit_cast(bf16x8_t, l)};
+    }
+    static __device__ __forceinline__ f32x16_t mma16(bf16x8_t a, bf16x8_t b, const f32x16_t &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // 16 terms of a product in fp32 accuracy from split operands (small terms first)
+    static __device__ __forceinline__ f32x16_t mma_x3(const Split8 &a, const Split8 &b, f32x16_t c) {
+        c = mma16(a.l, b.h, c);
+        c = mma16(a.h, b.l, c);
+        c = mma16(a.m, b.m, c);
+        c = mma16(a.m, b.h, c);
+        c = mma16(a.h, b.m, c);
+        return mma16(a.h, b.h, c);
     }
     // LDS offset (floats, within a region) of state entry x: rows e of M values, then z
     static __device__ __forceinline__ int lds_of(int x) {
@@ -231,13 +278,20 @@ struct LinScan {
         }
 
         // block state phi(K)^T V and key sum into this wave's region
+        // (16 terms per bf16 product: lane half h gives tokens tok(8 kb + i), i = 0 .. 7)
+        Split8 vs[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) vs[mb][kb] = split8(&vf[16 * mb + 8 * kb]);
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb) {
+            const Split8 ks0 = split8(&kt[16 * eb]), ks1 = split8(&kt[16 * eb + 8]);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 f32x16_t d = {};
-#pragma unroll
-                for (int r = 0; r < 16; ++r) d = mma(kt[16 * eb + r], vf[16 * mb + r], d);
+                d = mma_x3(ks0, vs[mb][0], d);
+                d = mma_x3(ks1, vs[mb][1], d);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     lds4(reg, (32 * mb + c) * EP + 32 * eb + 8 * g + 4 * h) =
@@ -252,7 +306,7 @@ struct LinScan {
         // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
         f32x16_t at = {};
 #pragma unroll
-        for (int i = 0; i < EB * 16; ++i) at = mma(kf[i], qf[i], at);
+        for (int i = 0; i < EB * 2; ++i) at = mma_x3(split8(&kf[8 * i]), split8(&qf[8 * i]), at);
         float rs = 0.f;  // row sum of A for query T0 + c (keys up to the query)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -294,11 +348,16 @@ struct LinScan {
         __builtin_amdgcn_sched_barrier(0);
         // in-span outputs A V: lane = column 32 mb + c, register r = query T0 + tok(r)
         f32x16_t ov[MB];
+        {
+            const float af[16] = {at[0], at[1], at[2],  at[3],  at[4],  at[5],  at[6],  at[7],
+                                  at[8], at[9], at[10], at[11], at[12], at[13], at[14], at[15]};
+            const Split8 as0 = split8(&af[0]), as1 = split8(&af[8]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            ov[mb] = (f32x16_t){};
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ov[mb] = mma(at[r], vf[16 * mb + r], ov[mb]);
+            for (int mb = 0; mb < MB; ++mb) {
+                ov[mb] = (f32x16_t){};
+                ov[mb] = mma_x3(as0, split8(&vf[16 * mb]), ov[mb]);
+                ov[mb] = mma_x3(as1, split8(&vf[16 * mb + 8]), ov[mb]);
+            }
         }
         if (pub_agg) publish(a.flag_agg + (size_t)hh * a.S + j, a.epoch);
         // every flag this span needs (the previous group's inclusive prefix, the earlier
@@ -374,16 +433,21 @@ struct LinScan {
         __syncthreads();
 
         // outputs: + phi(Q) (exclusive prefix), over e in the order of qf
+        // (16 terms per bf16 product: lane half h gives e = 32 eb + 16 kk + 8 (j / 4) + 4 h
+        // + j % 4, j = 0 .. 7, which are qf[16 eb + 8 kk + j])
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-            for (int eb = 0; eb < EB; ++eb)
+            for (int kk = 0; kk < 2; ++kk) {
+                const Split8 qs = split8(&qf[16 * eb + 8 * kk]);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4_t bv = lds4(reg, (32 * mb + c) * EP + 32 * eb + 8 * g + 4 * h);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) ov[mb] = mma(qf[16 * eb + 4 * g + t], bv[t], ov[mb]);
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int o = (32 * mb + c) * EP + 32 * eb + 16 * kk + 4 * h;
+                    const f32x4_t b0 = lds4(reg, o), b1 = lds4(reg, o + 8);
+                    const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                    ov[mb] = mma_x3(qs, split8(bv), ov[mb]);
                 }
+            }
         float inv = 1.f;
         if (fm) {
             float d = 0.f;
