@@ -355,8 +355,8 @@ struct LinScan {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 ov[mb] = (f32x16_t){};
-                ov[mb] = mma_x3(as0, split8(&vf[16 * mb]), ov[mb]);
-                ov[mb] = mma_x3(as1, split8(&vf[16 * mb + 8]), ov[mb]);
+                ov[mb] = mma_x3(as0, vs[mb][0], ov[mb]);
+                ov[mb] = mma_x3(as1, vs[mb][1], ov[mb]);
             }
         }
         if (pub_agg) publish(a.flag_agg + (size_t)hh * a.S + j, a.epoch);
