@@ -386,19 +386,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    wall, kernel_ms = time_steps(step, args.steps, 0)
     avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
     flops = 2.5 * w.flops if bwd else w.flops
@@ -518,24 +507,27 @@ def bench_linear(args, lw):
 
 
 def time_steps(step, steps: int, warmup: int):
-    """Warmup, then `steps` timed calls: wall seconds and HIP-event ms per call on the
-    current stream (the stream the library is given)."""
+    """Warmup, then `steps` timed calls: wall seconds, and the average launch duration in
+    ms (one entry per call) from one pair of HIP events around the timed calls on the
+    current stream (the stream the library is given).  The calls run back to back, so
+    the average is kernel time plus the GPU's launch-to-launch gap; events around each
+    call would add their own gap to every call (about 10 us per call on a 0.2 ms
+    kernel)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         step()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, [start.elapsed_time(end) / steps] * steps
 
 
 def bench_masked(args, mw):
