@@ -175,6 +175,21 @@ def test_one_pass_spans_and_groups(shape, fm):
     check(q, k, v, fm, 1e-6, f"one-pass {shape}", True)
 
 
+@pytest.mark.parametrize("fm", [False, True])
+def test_one_pass_products_keep_fp32_accuracy(fm):
+    """The one-pass form's products run on bf16 matrix cores from three-part splits of
+    each fp32 operand.  Values on a large common offset (1000 + N(0, 1)) need all 24 bits
+    of each operand: with two parts (16 bits) the normalised outputs, weighted means near
+    1000, would be off by ~2^-16 of their size (1.5e-5); with three they stay at fp32 level
+    (below 2e-6 relative, asserted) and within the fp32 bound.  Queries and keys at std 3
+    widen the range of phi as well."""
+    q, k, v = inputs(1, 2, 700, 64, 64, seed=31, std=3.0)
+    v = v + 1000.0
+    o, o_ref, err = check(q, k, v, fm, 1e-6, "one-pass, values offset by 1000", True)
+    if fm:  # a weighted mean of values near 1000: fp32-level relative accuracy
+        assert (err / np.abs(o_ref)).max() <= 2e-6
+
+
 def test_one_pass_repeats_bitwise_and_ignores_stale_workspace():
     """The look-back reads earlier spans in a fixed order, so repeated calls give the same
     bits whatever their timing; a workspace left by another call (other sizes, other
