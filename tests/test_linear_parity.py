@@ -175,6 +175,17 @@ def test_one_pass_spans_and_groups(shape, fm):
     check(q, k, v, fm, 1e-6, f"one-pass {shape}", True)
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 1, 32, 32), (1, 1, 127, 64, 32), (1, 1, 128, 32, 64),
+                                   (1, 1, 129, 64, 64), (4, 64, 256, 64, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_one_pass_edges(shape):
+    """One token; one span short of, exactly and one past 128 tokens (a single span, then a
+    ragged second one); and 256 heads of two spans (a grid of 512 workgroups, every head
+    class full)."""
+    q, k, v = inputs(*shape, seed=sum(shape) + 5)
+    check(q, k, v, True, 1e-6, f"one-pass edge {shape}", True)
+
+
 @pytest.mark.parametrize("fm", [False, True])
 def test_one_pass_products_keep_fp32_accuracy(fm):
     """The one-pass form's products run on bf16 matrix cores from three-part splits of
