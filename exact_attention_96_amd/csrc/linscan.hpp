@@ -247,13 +247,11 @@ struct LinScan {
                     for (int u = 0; u < 4; ++u) qf[16 * eb + 4 * i + u] = x[u];
                 }
         }
-        if (fm) {
+        // phi of K now (its loads were issued first); phi of Q just before A^T, so that the
+        // K transposition and the state product need not wait for Q
+        if (fm)
 #pragma unroll
-            for (int i = 0; i < EB * 16; ++i) {
-                qf[i] = phi(qf[i]);
-                kf[i] = phi(kf[i]);
-            }
-        }
+            for (int i = 0; i < EB * 16; ++i) kf[i] = phi(kf[i]);
         float *reg = lds + w * REG;
         {
             // kt is kf transposed, through this wave's LDS region (free until its state is
@@ -303,6 +301,10 @@ struct LinScan {
             zs += __shfl_xor(zs, 32);
             if (h == 0) reg[M * EP + 32 * eb + c] = zs;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (fm)
+#pragma unroll
+            for (int i = 0; i < EB * 16; ++i) qf[i] = phi(qf[i]);
         // A^T (keys x queries) of the diagonal block: lane = query T0 + c, register r = key tok(r)
         f32x16_t at = {};
 #pragma unroll
