@@ -281,7 +281,8 @@ ATTN_API int attn_bwd_noalloc(const void *q, const void *k, const void *v, const
  *              in-span products and the span's state (phi(K)^T V, key sum), then
  *              the prefix of the earlier spans taken from the workspace in a fixed
  *              order (spans publish their states there with flags), then
- *              phi(Q) times the prefix (fp32 matrix cores);
+ *              phi(Q) times the prefix (products on the bf16 matrix cores from
+ *              three-part bf16 splits of the fp32 operands: fp32-level accuracy);
  *            - otherwise: chunks of 64 tokens in three launches: per chunk
  *              phi(K)^T V and the key sum into the workspace, an exclusive prefix
  *              over the chunks, then each chunk's outputs (for E >= 32 on the fp32
