@@ -108,8 +108,8 @@ struct LinScan {
     static __device__ __forceinline__ f32x4_t ld4(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     }
-    static __device__ __forceinline__ void st(rsrc_t r, uint32_t off, float x) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
+    static __device__ __forceinline__ void st4(rsrc_t r, uint32_t off, f32x4_t x) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, (int)off, 0, 0);
     }
     // device-scope (sc1) 16-byte accesses: the stores write through, the loads are coherent
     static __device__ __forceinline__ f32x4_t ld4_dev(rsrc_t r, uint32_t off) {
@@ -464,18 +464,25 @@ struct LinScan {
             d += __shfl_xor(d, 32);
             inv = 1.f / (d + rs + a.eps);
         }
-        // (store offsets from a lane id taken here, so that the compiler does not keep the
-        // load offsets of the start alive until now)
-        const uint32_t ln = lane_now(), oc = ln & 31, oh = ln >> 5;
+        // Outputs through this wave's LDS region (its prefix state and key sum have been
+        // read): the accumulators (lane = column, registers = rows) become rows of OP
+        // floats, then each lane scales and stores 16-byte pieces of whole rows.  (Row pitch
+        // M + 8: the lane halves write rows 4 apart, on the two halves of the banks.)
+        constexpr int OP = M + 8, PIECES = TS * M / 4 / 64;
+        static_assert(TS * OP <= REG, "the output rows fit in a wave's region");
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float x = fm ? ov[mb][r] * __shfl(inv, row) : ov[mb][r];
-                const uint32_t orow = (uint32_t)(T0 + 8 * (r >> 2) + (r & 3)) + 4 * oh;
-                st(ro, (orow * M + 32 * mb + oc) * 4, x);
-            }
+            for (int r = 0; r < 16; ++r) reg[(8 * (r >> 2) + 4 * h + (r & 3)) * OP + 32 * mb + c] = ov[mb][r];
+        // (store offsets from a lane id taken here, so that the compiler does not keep the
+        // load offsets of the start alive until now)
+        const uint32_t ln = lane_now();
+#pragma unroll
+        for (int p = 0; p < PIECES; ++p) {
+            const uint32_t q = ln + 64 * p, row = q / (M / 4), col = 4 * (q % (M / 4));
+            const f32x4_t x = lds4(reg, row * OP + col) * __shfl(inv, (int)row);  // (inv = 1 without the feature map)
+            st4(ro, ((uint32_t)(T0 + row) * M + col) * 4, x);
+        }
     }
 
     // workspace layout (bytes from the start; every part 256-byte aligned)
