@@ -184,9 +184,13 @@ struct LinScan {
         c = mma16(a.h, b.m, c);
         return mma16(a.h, b.h, c);
     }
-    // LDS offset (floats, within a region) of state entry x: rows e of M values, then z
-    static __device__ __forceinline__ int lds_of(int x) {
-        return x < E * M ? (x / E) * EP + x % E : M * EP + (x - E * M);
+    // LDS offset (floats, within a region) of piece x4 of a state and key sum, the order of
+    // the exchange (a thread's 16-byte accesses) and of the workspace slots: piece
+    // x4 = M p + m < E M / 4 holds entries e = 4 p .. 4 p + 3 of value column m, so that the
+    // consecutive pieces of a wave's lanes sit in consecutive rows, four banks apart; then
+    // the key sum
+    static __device__ __forceinline__ int lds_of4(int x4) {
+        return x4 < CH - E / 4 ? (x4 % M) * EP + 4 * (x4 / M) : M * EP + 4 * (x4 - (CH - E / 4));
     }
     static __device__ __forceinline__ f32x4_t &lds4(float *base, int o) { return *(f32x4_t *)(base + o); }
     static __device__ __forceinline__ rsrc_t rsrc_u64(const unsigned long long *p, int n) {
@@ -339,7 +343,7 @@ struct LinScan {
             const int x4 = tid + i * THREADS;
             ag[i] = (f32x4_t){};
             if (x4 < CH) {
-                const int o = lds_of(4 * x4);
+                const int o = lds_of4(x4);
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) ag[i] += lds4(lds, ww * REG + o);
             }
@@ -427,7 +431,7 @@ struct LinScan {
         for (int i = 0; i < PER; ++i) {
             const int x4 = tid + i * THREADS;
             if (x4 < CH) {
-                const int o = lds_of(4 * x4);
+                const int o = lds_of4(x4);
                 f32x4_t run = pr[i];
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
