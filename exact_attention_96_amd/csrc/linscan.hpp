@@ -263,26 +263,19 @@ struct LinScan {
             // the two halves of the banks
             constexpr int KP = E + 8;
             static_assert(TS * KP <= REG, "the phi(K) block fits in a wave's region");
-            // Row t keeps its 16-byte pieces in an order swizzled by bit 3 of t (pieces 2 k
-            // and 2 k + 1 swapped in rows 8 .. 15 and 24 .. 31), so that rows c and c + 8,
-            // written by lanes of one 16-lane group, start their pieces on different banks
-            // (E + 8 floats alone would put them on the same ones).  A column read of row
-            // tok(r) undoes it with e ^ 4 where (tok(r) >> 3) & 1 = (r >> 2) & 1.
-            const int sw = 4 * (h ^ ((c >> 3) & 1));
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    lds4(reg, c * KP + 32 * eb + 8 * i + sw) =
+                    lds4(reg, c * KP + 32 * eb + 8 * i + 4 * h) =
                         (f32x4_t){kf[16 * eb + 4 * i], kf[16 * eb + 4 * i + 1], kf[16 * eb + 4 * i + 2], kf[16 * eb + 4 * i + 3]};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 // phi(0) = 1: keys past N are zeroed
                 const float in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N ? 1.f : 0.f;
-                const int cr = c ^ (4 * ((r >> 2) & 1));
 #pragma unroll
                 for (int eb = 0; eb < EB; ++eb)
-                    kt[16 * eb + r] = reg[(8 * (r >> 2) + 4 * h + (r & 3)) * KP + 32 * eb + cr] * in;
+                    kt[16 * eb + r] = reg[(8 * (r >> 2) + 4 * h + (r & 3)) * KP + 32 * eb + c] * in;
             }
         }
 
