@@ -175,9 +175,11 @@ def _smi_gfx_clocks():
 
 
 def sustained_clock(step, seconds: float = 1.5):
-    """Median shader clock (MHz) over the XCDs, sampled with amd-smi while the same
-    step runs back to back for `seconds` right after the timed region (the timed region
-    itself is too short for the tool).  Returns a dict, or None without amd-smi."""
+    """Shader clock (MHz) sampled with amd-smi while the same step runs back to back for
+    `seconds` right after the timed region (the timed region itself is too short for the
+    tool): per sample the mean of the per-XCD readings (the chip's aggregate clock; the
+    highest reading is kept too), then the median over samples.  Returns a dict, or None
+    without amd-smi."""
     import threading
     import torch
     samples, stop = [], threading.Event()
@@ -192,22 +194,32 @@ def sustained_clock(step, seconds: float = 1.5):
     t = threading.Thread(target=poll, daemon=True)
     t0 = time.perf_counter()
     t.start()
+    # steps are enqueued back to back; the host waits only every ~20 ms of work, so the
+    # GPU does not idle between batches while it is sampled
+    ev = torch.cuda.Event()
     while time.perf_counter() - t0 < seconds or (t.is_alive() and not samples and time.perf_counter() - t0 < 15):
-        for _ in range(20):
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < 0.02:
             step()
-        torch.cuda.synchronize()
+        ev.record()
+        ev.synchronize()
+    torch.cuda.synchronize()
     stop.set()
     t.join(timeout=15)
-    if not samples:
+    # readings below the lowest active DPM level (500 MHz) are an idle XCD
+    kept = [[x for x in c if x >= 500.0] for c in samples]
+    kept = [c for c in kept if c]
+    if not kept:
         return None
-    # readings below the lowest active DPM level (500 MHz) are an idle XCD between batches
-    flat = sorted(x for c in samples for x in c if x >= 500.0)
-    if not flat:
-        return None
-    return {"mhz_median": flat[len(flat) // 2], "mhz_min": flat[0], "mhz_max": flat[-1],
-            "samples": len(samples),
+    mean = sorted(sum(c) / len(c) for c in kept)
+    top = sorted(max(c) for c in kept)
+    low = sorted(min(c) for c in kept)
+    return {"mhz_median": round(mean[len(mean) // 2], 1), "mhz_min": mean[0], "mhz_max": mean[-1],
+            "mhz_fastest_xcd_median": top[len(top) // 2], "mhz_slowest_xcd_median": low[len(low) // 2],
+            "samples": len(kept),
             "source": "amd-smi metric --clock (per-XCD gfx clocks) polled while the step repeats for "
-                      f"{seconds:.1f} s right after the timed region"}
+                      f"{seconds:.1f} s right after the timed region; per sample the mean over the XCDs, "
+                      "median over samples"}
 
 
 def cpu_baseline(w, q, k, v, seconds: float):
