@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3] [--pass fwd|bwd]
 
+(The short launches l1, c1, c2 and c4 default to 200 warm-up and 200 timed steps.)
+
 A step is one call of attn_fwd (the whole fused forward: Q tile load, K/V
 staging, both matrix products, online softmax, normalisation, O and lse
 stores) over one batch of seeded synthetic inputs already resident in HBM.
