@@ -25,6 +25,11 @@ attention, fp32; with E = M = 64 the one-pass form: per 128-token span its own
 products and state, the prefix of the earlier spans through the workspace, the
 outputs; the workspace is allocated before timing), bound by HBM: the value is
 algorithmic GB/s (read q, k, v and write o once) against the 8 TB/s peak.
+
+With --probes it runs only the rate probes of libattn_probe.so (dense bf16 MFMA on
+random and on constant operands; LDS reads as ds_read_b128, ds_read_b64 and
+ds_read_b64_tr_b16) and prints one JSON line: each probe's rate, the shader clock
+amd-smi reads while it runs, and the rate per compute unit and clock.
 """
 from __future__ import annotations
 
@@ -311,6 +316,83 @@ def copy_probe(nbytes: int, steps: int):
                       "steps": steps}), flush=True)
 
 
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "exact_attention_96_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m exact_attention_96_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.attn_probe_mfma_bf16.argtypes = [vp, vp, ci, ci, vp]
+    lib.attn_probe_lds_read.argtypes = [vp, ci, ci, ci, vp]
+    return lib
+
+
+def _probe_rate(launch, units_per_launch: float, seconds: float, clock_seconds: float):
+    """Launches back to back for `seconds` (warm-up: the board settles at its clock for
+    the load), then times 20 launches with one event pair; then the clock while the
+    same launches repeat.  Returns (units per second, clock dict or None)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        launch()
+        torch.cuda.synchronize()
+    _, ms = time_steps(launch, 20, 0)
+    rate = units_per_launch / (ms[0] * 1e-3)
+    clock = sustained_clock(launch, clock_seconds) if clock_seconds > 0 else None
+    return rate, clock
+
+
+def run_probes(clock_seconds: float) -> None:
+    """Sustained rates of the matrix cores and of LDS reads on this board (one JSON line).
+    The published peaks assume the 2.4 GHz peak clock; under load the board holds a
+    power-limited clock, and what a compute unit does per clock at that clock is what
+    the attention kernels can be held to."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"probes": {}, "cus": cus, "device": torch.cuda.get_device_name(0)}
+    # matrix cores: 1024 workgroups of 4 waves (two per SIMD), 2048 iterations of 8 products
+    blocks, iters = 1024, 2048
+    flops = blocks * 4 * iters * 8 * 32 * 32 * 16 * 2
+    res = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    g = torch.Generator().manual_seed(20260101)
+    operands = {"mfma_bf16_random": torch.randn(256 * 8 * 8, generator=g).to(torch.bfloat16),
+                "mfma_bf16_ones": torch.ones(256 * 8 * 8, dtype=torch.bfloat16)}
+    for name, ops in operands.items():
+        opd = ops.to("cuda:0")
+
+        def launch():
+            rc = lib.attn_probe_mfma_bf16(opd.data_ptr(), res.data_ptr(), blocks, iters, stream)
+            assert rc == 0, rc
+        rate, clock = _probe_rate(launch, flops, 1.0, clock_seconds)
+        tf = rate / 1e12
+        entry = {"tflops": round(tf, 1), "frac_of_2516_6": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
+        if clock:
+            entry["clock"] = clock
+            entry["flop_per_clk_per_cu"] = round(rate / (cus * clock["mhz_median"] * 1e6), 1)
+        out["probes"][name] = entry
+        print(f"[probe] {name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
+    # LDS reads: 2048 workgroups of 8 waves with 64 KiB of LDS each (two per CU at a time)
+    blocks, iters = 2048, 512
+    resu = torch.empty(blocks * 512, dtype=torch.int32, device="cuda:0")
+    for mode, (name, piece) in enumerate((("lds_read_b128", 16), ("lds_read_b64", 8), ("lds_read_b64_tr_b16", 8))):
+        nbytes = blocks * 512 * iters * 8 * piece
+
+        def launch():
+            rc = lib.attn_probe_lds_read(resu.data_ptr(), blocks, iters, mode, stream)
+            assert rc == 0, rc
+        rate, clock = _probe_rate(launch, nbytes, 1.0, clock_seconds)
+        entry = {"tb_per_s": round(rate / 1e12, 2)}
+        if clock:
+            entry["clock"] = clock
+            entry["bytes_per_clk_per_cu"] = round(rate / (cus * clock["mhz_median"] * 1e6), 1)
+        out["probes"][name] = entry
+        print(f"[probe] {name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +413,8 @@ def main():
                     help="seconds of repeated steps while amd-smi samples the shader clock (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of this many bytes (counter calibration)")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the matrix-core and LDS rate probes (libattn_probe.so)")
     ap.add_argument("--summarize-traffic", action="store_true",
                     help="write the HBM traffic summary from rocprofv3 counter CSVs and exit")
     ap.add_argument("--fetch-csv")
@@ -363,6 +447,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    if args.probes:
+        run_probes(args.clock_seconds)
         return
     if args.workload in LINEAR_WORKLOADS:
         if args.which != "fwd":

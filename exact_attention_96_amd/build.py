@@ -1,9 +1,10 @@
-"""Builds libattn.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Builds libattn.so (the HIP kernels and the C ABI) in-tree for gfx950, and
+libattn_probe.so (the measurement harness's rate probes, include/attn_probe.h).
 
     python -m exact_attention_96_amd.build [-v]
 
-Always recompiles.  The library is written next to this file, where the
-Python binding loads it from.
+Always recompiles.  The libraries are written next to this file, where the
+Python binding and bench.py load them from.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = [os.path.join(CSRC, "attn_api.hip")]
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+PROBE_SOURCES = [os.path.join(PKG, "probe", "probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
@@ -33,9 +36,10 @@ HIP_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB,
+          sources: list[str] | None = None) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *(sources or SOURCES), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,5 +54,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    return build(verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
