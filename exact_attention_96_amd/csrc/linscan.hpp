@@ -123,9 +123,10 @@ struct LinScan {
     // v_exp_f32, times (1 + tl ln 2): a few operations instead of the library expf's
     // range reduction.  Measured on gfx950 against fp64 exp over x in [-87, 0]: at most
     // 1.26 ulp (the library expf: 0.85 ulp); results below the normal range flush to 0.
-    // Written as e^min(x, 0) + max(x, 0) (the exponential of 0 is exactly 1, so x > 0
-    // still gets x + 1), with no branch: a conditional exponential compiles to a branch
-    // per element.  A NaN x gives NaN.
+    // Written as e^xn (1 + tl ln 2) + (x - xn) with xn = min(x, 0), with no branch (a
+    // conditional exponential compiles to a branch per element): for x > 0 the
+    // exponential of 0 is exactly 1 and x - xn = x, one rounding of x + 1; otherwise
+    // x - xn is exactly 0.  A NaN x gives NaN.
     static __device__ __forceinline__ float phi(float x) {
         const float c_hi = 1.44269502162933349609375f;  // log2(e) rounded to float
         const float c_lo = 1.92596298909109e-8f;        // log2(e) - c_hi
@@ -134,7 +135,7 @@ struct LinScan {
         const float th = xn * c_hi;
         const float tl = fmaf(xn, c_hi, -th) + xn * c_lo;
         const float e = __builtin_amdgcn_exp2f(th);
-        return fmaf(e, tl * 0.69314718055994530942f, e) + (pos ? x : 0.f);
+        return fmaf(e, tl * 0.69314718055994530942f, e + (x - xn));
     }
     // lane id (0..63) computed where it is used (volatile: not hoisted, not shared with
     // earlier uses)
@@ -270,13 +271,15 @@ struct LinScan {
                     lds4(reg, c * KP + 32 * eb + 8 * i + 4 * h) =
                         (f32x4_t){kf[16 * eb + 4 * i], kf[16 * eb + 4 * i + 1], kf[16 * eb + 4 * i + 2], kf[16 * eb + 4 * i + 3]};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // phi(0) = 1: keys past N are zeroed
-                const float in = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r)
 #pragma unroll
-                for (int eb = 0; eb < EB; ++eb)
-                    kt[16 * eb + r] = reg[(8 * (r >> 2) + 4 * h + (r & 3)) * KP + 32 * eb + c] * in;
-            }
+                for (int eb = 0; eb < EB; ++eb) kt[16 * eb + r] = reg[(8 * (r >> 2) + 4 * h + (r & 3)) * KP + 32 * eb + c];
+            if (T0 + TS > N)  // phi(0) = 1: keys past N are zeroed (a wave at the sequence end)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int eb = 0; eb < EB; ++eb)
+                        kt[16 * eb + r] = T0 + 8 * (r >> 2) + 4 * h + (r & 3) < N ? kt[16 * eb + r] : 0.f;
         }
 
         // block state phi(K)^T V and key sum into this wave's region
@@ -408,11 +411,11 @@ struct LinScan {
                     const int x4 = tid + i * THREADS;
                     t[u][i] = ld4_dev(rag, k0 + u < j && x4 < CH ? (uint32_t)((k0 + u) * ENT + 4 * x4) * 4 : kOut);
                 }
+            // (slots past j - 1 were read at kOut: zeros)
 #pragma unroll
             for (int u = 0; u < NB; ++u)
 #pragma unroll
-                for (int i = 0; i < PER; ++i)
-                    if (k0 + u < j) pr[i] += t[u][i];
+                for (int i = 0; i < PER; ++i) pr[i] += t[u][i];
         }
         if (!ok)
 #pragma unroll
