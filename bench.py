@@ -26,6 +26,10 @@ products and state, the prefix of the earlier spans through the workspace, the
 outputs; the workspace is allocated before timing), bound by HBM: the value is
 algorithmic GB/s (read q, k, v and write o once) against the 8 TB/s peak.
 
+The MFMA-bound lines also report, under roofline.practical_ceiling, this board's dense bf16
+MFMA rate on random operands (the probe below, run for --practical-seconds right after the
+bench) and the kernel's fraction of it.
+
 With --probes it runs only the rate probes of libattn_probe.so (dense bf16 MFMA on
 random and on constant operands; LDS reads as ds_read_b128, ds_read_b64 and
 ds_read_b64_tr_b16) and prints one JSON line: each probe's rate, the shader clock
@@ -393,6 +397,30 @@ def run_probes(clock_seconds: float) -> None:
     print(json.dumps(out), flush=True)
 
 
+def practical_ceiling(seconds: float):
+    """This board's dense bf16 MFMA rate on random operands (libattn_probe.so, the probe of
+    --probes), launched back to back for `seconds` and then timed: the most a bf16 kernel
+    with real data reaches here at the clock the board holds under that load.  None
+    without the probe library."""
+    import torch
+    try:
+        lib = _probe_lib()
+    except (RuntimeError, OSError):
+        return None
+    blocks, iters = 1024, 2048
+    flops = blocks * 4 * iters * 8 * 32 * 32 * 16 * 2
+    res = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    g = torch.Generator().manual_seed(20260101)
+    ops = torch.randn(256 * 8 * 8, generator=g).to(torch.bfloat16).to("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.attn_probe_mfma_bf16(ops.data_ptr(), res.data_ptr(), blocks, iters, stream)
+        assert rc == 0, rc
+    rate, _ = _probe_rate(launch, flops, seconds, 0.0)
+    return rate / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +437,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle runs whole heads for cpu_baseline (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=None, help="(0: skip the cpu_baseline leg)")
+    ap.add_argument("--practical-seconds", type=float, default=1.0,
+                    help="seconds of the random-operand MFMA probe for the practical ceiling "
+                         "of the MFMA-bound lines (0: skip)")
     ap.add_argument("--clock-seconds", type=float, default=1.5,
                     help="seconds of repeated steps while amd-smi samples the shader clock (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -544,6 +575,15 @@ def main():
             clk["peak_at_clock_tflops"] = round(peak_at, 1)
             clk["frac_at_clock"] = round(achieved / peak_at, 4)
         out["roofline"]["sustained_clock"] = clk
+    if args.practical_seconds > 0 and w.dtype != "f32":
+        print(f"[bench] practical ceiling: MFMA probe for ~{args.practical_seconds:.1f} s", file=sys.stderr,
+              flush=True)
+        pc = practical_ceiling(args.practical_seconds)
+        if pc is not None:
+            out["roofline"]["practical_ceiling"] = {
+                "tflops": round(pc, 1), "frac": round(achieved / pc, 4),
+                "source": "dense bf16 v_mfma_f32_32x32x16 on every SIMD with random operands "
+                          "(libattn_probe.so), timed on this board right after the bench"}
     if args.cpu_seconds > 0 and args.cpu_heads != 0:
         print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds) if bwd else
