@@ -105,6 +105,16 @@ def test_causal_tile_orders(B, H):
     full_parity(q, k, v, True, 1.0 / math.sqrt(128), "bf16", f"B={B} H={H} N=700")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_round_robin_lists(d, causal):
+    """33 heads (not a multiple of 8: the jobs are dealt round robin over the grid, not per
+    XCD) and 17 query tiles (an odd count: the causal middle tile has no partner), so that
+    more jobs than compute units leave several jobs to some workgroups; a ragged tail."""
+    q, k, v = random_qkv(3, 11, 4196, d, "bf16", seed=60 + d + int(causal))
+    full_parity(q, k, v, causal, 1.0 / math.sqrt(d), "bf16", f"B=3 H=11 N=4196 d={d}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_many_heads_short(dtype):
     q, k, v = random_qkv(8, 40, 96, 64, dtype, seed=7)
